@@ -1,0 +1,386 @@
+/*
+ * CPU oracle for the 8-bit (SageAttention-form) attention forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or helper with the HIP path under bit_quantized_exact_amd/.
+ *
+ * It is deliberately plain and slow: fp64 loops, two-pass softmax, no tiling,
+ * no online rescaling, no blocking beyond what the definitions state.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [MHA-GQA]  "注意力即一切：从 MHA 到 GQA" (bojinhu.xyz):
+ *              §2.2 (the four steps of attention), §2.3 (causal mask),
+ *              §4.1 (MQA), §5.1 (GQA grouping).
+ *   [SA]       "又快又准，即插即用！清华8比特量化Attention，两倍加速于
+ *              FlashAttention2…" (SageAttention, 17aitech reprint of a
+ *              jiqizhixin article), section 技术方案 ("technical approach"):
+ *              K smoothing, per-block INT8 Q/K, INT8 QK^T with INT32
+ *              accumulation, FP16 P and V.
+ *   [FA-guide] "FlashAttention" guide (aiunderstanding.org): FAQ on exactness.
+ *
+ * Readings taken where the pages leave a step open (each also listed in the
+ * design notes of the repository):
+ *   - mean(K) is the per-channel mean over all tokens of one (batch, kv-head),
+ *     the only reading under which [SA]'s claimed invariance
+ *     softmax(QK^T) = softmax(Q(K-mean K)^T) holds.
+ *   - The channel sum is exact; it is rounded once to fp64, divided by S in
+ *     fp64 and rounded to fp32.
+ *   - Block quantisation is symmetric absmax: a = max|x|, r = 127/a (fp32,
+ *     round-to-nearest-even), q = clamp(rint(x*r), -127, 127), delta = a/127.
+ *     An all-zero block gives q = 0, delta = 0.
+ *   - Q is not smoothed.  1/sqrt(D) is applied at dequantisation, not folded
+ *     into Q before quantisation.
+ *   - Causal means key j is visible to query i iff j <= i (one sequence length).
+ *   - A row with no visible key (cannot happen for square causal) gives O = 0
+ *     and lse = -inf.
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off -fno-fast-math -shared -fPIC.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <omp.h>
+
+/* ------------------------------------------------------------------------ */
+/* IEEE binary16 decoding (from the format definition: 1 sign bit, 5       */
+/* exponent bits with bias 15, 10 fraction bits; exponent 0 = subnormal,    */
+/* exponent 31 = inf/nan).                                                  */
+/* ------------------------------------------------------------------------ */
+double oracle_half_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int expo = (h >> 10) & 0x1f;
+    int frac = h & 0x3ff;
+    double v;
+    if (expo == 0) {
+        v = ldexp((double)frac, -24);                 /* frac * 2^-10 * 2^-14 */
+    } else if (expo == 31) {
+        v = frac ? NAN : INFINITY;
+    } else {
+        v = ldexp((double)(1024 + frac), expo - 25);  /* 1.frac * 2^(e-15)   */
+    }
+    return sign ? -v : v;
+}
+
+void oracle_half_array_to_double(const uint16_t* h, double* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_half_to_double(h[i]);
+}
+
+/* Round a finite double to the nearest binary16 value (ties to even),
+ * returned as a double.  Values beyond the fp16 range saturate to +-inf. */
+double oracle_round_to_half(double x)
+{
+    if (x == 0.0 || !isfinite(x)) return x;
+    double ax = fabs(x);
+    int e;
+    frexp(ax, &e);                 /* ax = m * 2^e, m in [0.5, 1) */
+    int ulp_exp = (e - 1) - 10;    /* 11 significant bits in the normal range */
+    if (ulp_exp < -24) ulp_exp = -24;  /* subnormal spacing */
+    double r = ldexp(rint(ldexp(ax, -ulp_exp)), ulp_exp);
+    if (r > 65504.0) r = INFINITY;
+    return x < 0 ? -r : r;
+}
+
+static double* decode_all(const uint16_t* h, int64_t n)
+{
+    double* d = (double*)malloc((size_t)n * sizeof(double));
+    if (!d) return NULL;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) d[i] = oracle_half_to_double(h[i]);
+    return d;
+}
+
+static int check_map(int Hq, int Hkv, const int32_t* kv_map)
+{
+    for (int h = 0; h < Hq; ++h)
+        if (kv_map[h] < 0 || kv_map[h] >= Hkv) return -4;
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* O1: exact attention in fp64 ([MHA-GQA] §2.2, §2.3, §5.1).                */
+/*   s_ij = sm_scale * sum_c Q[b,h,i,c] K[b,map[h],j,c]  (visible j only)   */
+/*   p_ij = exp(s_ij - max_j s_ij), l_i = sum_j p_ij                        */
+/*   O[b,h,i,:] = sum_j p_ij V[b,map[h],j,:] / l_i ; lse_i = m_i + ln l_i   */
+/* rows: query rows to evaluate for every (b,h) (NULL = all S rows).        */
+/* out: [B, Hq, nrows, D] fp64; lse: [B, Hq, nrows] or NULL.                */
+/* ------------------------------------------------------------------------ */
+int oracle_attention(int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t D,
+                     const uint16_t* q_f16, const uint16_t* k_f16, const uint16_t* v_f16,
+                     const int32_t* kv_map, int32_t causal, double sm_scale,
+                     const int32_t* rows, int32_t nrows,
+                     double* out, double* lse, int32_t nthreads)
+{
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || D <= 0) return -1;
+    if (check_map(Hq, Hkv, kv_map)) return -4;
+    if (!rows) nrows = S;
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+
+    int64_t nkv = (int64_t)B * Hkv * S * D;
+    double* K = decode_all(k_f16, nkv);
+    double* V = decode_all(v_f16, nkv);
+    if (!K || !V) { free(K); free(V); return -5; }
+
+    int64_t total = (int64_t)B * Hq * nrows;
+    int status = 0;
+#pragma omp parallel
+    {
+        double* s = (double*)malloc((size_t)S * sizeof(double));
+        double* qrow = (double*)malloc((size_t)D * sizeof(double));
+        double* acc = (double*)malloc((size_t)D * sizeof(double));
+        if (!s || !qrow || !acc) {
+#pragma omp atomic write
+            status = -5;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t t = 0; t < total; ++t) {
+                int64_t bh = t / nrows;
+                int32_t r = (int32_t)(t % nrows);
+                int32_t i = rows ? rows[r] : r;
+                int32_t b = (int32_t)(bh / Hq), h = (int32_t)(bh % Hq);
+                int32_t kh = kv_map[h];
+                const uint16_t* qp = q_f16 + (((int64_t)b * Hq + h) * S + i) * D;
+                const double* Kh = K + ((int64_t)b * Hkv + kh) * S * D;
+                const double* Vh = V + ((int64_t)b * Hkv + kh) * S * D;
+                double* o = out + t * D;
+                for (int c = 0; c < D; ++c) qrow[c] = oracle_half_to_double(qp[c]);
+
+                int32_t nvis = causal ? (i + 1 < S ? i + 1 : S) : S;
+                if (nvis <= 0) {
+                    for (int c = 0; c < D; ++c) o[c] = 0.0;
+                    if (lse) lse[t] = -INFINITY;
+                    continue;
+                }
+                /* pass 1: scores and their maximum */
+                double m = -INFINITY;
+                for (int32_t j = 0; j < nvis; ++j) {
+                    double dot = 0.0;
+                    for (int c = 0; c < D; ++c) dot += qrow[c] * Kh[(int64_t)j * D + c];
+                    s[j] = dot * sm_scale;
+                    if (s[j] > m) m = s[j];
+                }
+                /* pass 2: weights, their sum and the weighted sum of V */
+                double l = 0.0;
+                for (int c = 0; c < D; ++c) acc[c] = 0.0;
+                for (int32_t j = 0; j < nvis; ++j) {
+                    double p = exp(s[j] - m);
+                    l += p;
+                    for (int c = 0; c < D; ++c) acc[c] += p * Vh[(int64_t)j * D + c];
+                }
+                for (int c = 0; c < D; ++c) o[c] = acc[c] / l;
+                if (lse) lse[t] = m + log(l);
+            }
+        }
+        free(s); free(qrow); free(acc);
+    }
+    free(K); free(V);
+    return status;
+}
+
+/* ------------------------------------------------------------------------ */
+/* O2: K channel mean over tokens ([SA] 技术方案, K smoothing).             */
+/*   sum_c = sum over all S tokens of K[b,k,:,c], accumulated in fp64.      */
+/*   Every fp16 value is an integer multiple of 2^-24, so the fp64 sum is   */
+/*   exact while every partial sum stays below 2^29 in magnitude; the       */
+/*   function checks sum_j |K| < 2^29 per channel and returns -4 if not.    */
+/*   mu_c = (float)(sum_c / S) : one fp64 division, then RNE to fp32.       */
+/* ------------------------------------------------------------------------ */
+int oracle_k_mean(int32_t B, int32_t Hkv, int32_t S, int32_t D,
+                  const uint16_t* k_f16, float* mu)
+{
+    if (B <= 0 || Hkv <= 0 || S <= 0 || D <= 0) return -1;
+    int status = 0;
+    for (int64_t bk = 0; bk < (int64_t)B * Hkv; ++bk) {
+        const uint16_t* Kh = k_f16 + bk * S * D;
+        for (int c = 0; c < D; ++c) {
+            double sum = 0.0, sabs = 0.0;
+            for (int32_t j = 0; j < S; ++j) {
+                double x = oracle_half_to_double(Kh[(int64_t)j * D + c]);
+                sum += x;
+                sabs += fabs(x);
+            }
+            if (!(sabs < 536870912.0)) status = -4;   /* 2^29 */
+            mu[bk * D + c] = (float)(sum / (double)S);
+        }
+    }
+    return status;
+}
+
+/* Smoothed K in fp32: ks = (float)K - mu  (one fp32 subtraction).          */
+void oracle_smooth_k(int32_t B, int32_t Hkv, int32_t S, int32_t D,
+                     const uint16_t* k_f16, const float* mu, float* ks)
+{
+    for (int64_t bk = 0; bk < (int64_t)B * Hkv; ++bk)
+        for (int32_t j = 0; j < S; ++j)
+            for (int c = 0; c < D; ++c) {
+                int64_t idx = (bk * S + j) * D + c;
+                float x = (float)oracle_half_to_double(k_f16[idx]);
+                ks[idx] = x - mu[bk * D + c];
+            }
+}
+
+/* fp16 -> fp32 widening of a whole array (exact).                          */
+void oracle_half_array_to_float(const uint16_t* h, float* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = (float)oracle_half_to_double(h[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* O3: per-block symmetric INT8 quantisation ([SA] 技术方案: Q and K are    */
+/* quantised to INT8 with one scale per FlashAttention-sized block).        */
+/* x: [nmat, S, D] fp32.  Block b covers rows [b*block, min(S,(b+1)*block)) */
+/* of one matrix (the last block may be partial).                           */
+/* q: [nmat, S, D] int8;  scale: [nmat, ceil(S/block)] fp32.                */
+/* ------------------------------------------------------------------------ */
+void oracle_quant_blocks(int64_t nmat, int32_t S, int32_t D, int32_t block,
+                         const float* x, int8_t* q, float* scale)
+{
+    int32_t nblk = (S + block - 1) / block;
+    for (int64_t mtx = 0; mtx < nmat; ++mtx) {
+        for (int32_t bi = 0; bi < nblk; ++bi) {
+            int32_t r0 = bi * block, r1 = r0 + block < S ? r0 + block : S;
+            const float* xb = x + (mtx * S + r0) * D;
+            int8_t* qb = q + (mtx * S + r0) * D;
+            int64_t n = (int64_t)(r1 - r0) * D;
+            float a = 0.0f;
+            for (int64_t e = 0; e < n; ++e) {
+                float v = fabsf(xb[e]);
+                if (v > a) a = v;
+            }
+            if (a == 0.0f) {
+                for (int64_t e = 0; e < n; ++e) qb[e] = 0;
+                scale[mtx * nblk + bi] = 0.0f;
+                continue;
+            }
+            float r = 127.0f / a;
+            for (int64_t e = 0; e < n; ++e) {
+                float t = rintf(xb[e] * r);
+                if (t > 127.0f) t = 127.0f;
+                if (t < -127.0f) t = -127.0f;
+                qb[e] = (int8_t)t;
+            }
+            scale[mtx * nblk + bi] = a / 127.0f;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Integer scores ([SA] 技术方案: INT8 QK^T with an INT32 accumulator).     */
+/*   S32[b,h,i,j] = sum_c q[b,h,i,c] * k[b,map[h],j,c], exact in int64,     */
+/*   then checked to fit in int32.  Entries with j > i under the causal     */
+/*   mask are set to `fill`.  s_out: [B, Hq, nrows, S].                     */
+/* ------------------------------------------------------------------------ */
+int oracle_scores_i32(int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t D,
+                      const int8_t* q_i8, const int8_t* k_i8, const int32_t* kv_map,
+                      int32_t causal, const int32_t* rows, int32_t nrows,
+                      int32_t* s_out, int32_t fill)
+{
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || D <= 0) return -1;
+    if (check_map(Hq, Hkv, kv_map)) return -4;
+    if (!rows) nrows = S;
+    int status = 0;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < (int64_t)B * Hq * nrows; ++t) {
+        int64_t bh = t / nrows;
+        int32_t r = (int32_t)(t % nrows);
+        int32_t i = rows ? rows[r] : r;
+        int32_t b = (int32_t)(bh / Hq), h = (int32_t)(bh % Hq);
+        const int8_t* qp = q_i8 + (((int64_t)b * Hq + h) * S + i) * D;
+        const int8_t* kp = k_i8 + ((int64_t)b * Hkv + kv_map[h]) * S * D;
+        for (int32_t j = 0; j < S; ++j) {
+            if (causal && j > i) { s_out[t * S + j] = fill; continue; }
+            int64_t dot = 0;
+            for (int c = 0; c < D; ++c) dot += (int64_t)qp[c] * (int64_t)kp[(int64_t)j * D + c];
+            if (dot > INT32_MAX || dot < INT32_MIN) {
+#pragma omp atomic write
+                status = -4;
+            }
+            s_out[t * S + j] = (int32_t)dot;
+        }
+    }
+    return status;
+}
+
+/* ------------------------------------------------------------------------ */
+/* O4: the quantised-attention model (diagnostic).  Exact softmax attention */
+/* whose scores are the dequantised integer scores                          */
+/*   s_ij = S32_ij * dQ[i/BQ] * dK[j/BK] * sm_scale          (fp64)         */
+/* and whose weights enter the P.V product rounded to fp16 ([SA] 技术方案:  */
+/* P and V stay FP16).  The row sum l uses the unrounded weights when       */
+/* l_from_rounded == 0 and the fp16-rounded ones otherwise.                 */
+/* ------------------------------------------------------------------------ */
+int oracle_quant_attention(int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t D,
+                           const int8_t* q_i8, const float* q_scale, int32_t bq,
+                           const int8_t* k_i8, const float* k_scale, int32_t bk,
+                           const uint16_t* v_f16, const int32_t* kv_map,
+                           int32_t causal, double sm_scale, int32_t l_from_rounded,
+                           const int32_t* rows, int32_t nrows,
+                           double* out, double* lse, int32_t nthreads)
+{
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || D <= 0 || bq <= 0 || bk <= 0) return -1;
+    if (check_map(Hq, Hkv, kv_map)) return -4;
+    if (!rows) nrows = S;
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+    int32_t nbq = (S + bq - 1) / bq, nbk = (S + bk - 1) / bk;
+
+    int64_t nkv = (int64_t)B * Hkv * S * D;
+    double* V = decode_all(v_f16, nkv);
+    if (!V) return -5;
+    int64_t total = (int64_t)B * Hq * nrows;
+    int status = 0;
+#pragma omp parallel
+    {
+        double* s = (double*)malloc((size_t)S * sizeof(double));
+        double* acc = (double*)malloc((size_t)D * sizeof(double));
+        if (!s || !acc) {
+#pragma omp atomic write
+            status = -5;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t t = 0; t < total; ++t) {
+                int64_t bh = t / nrows;
+                int32_t r = (int32_t)(t % nrows);
+                int32_t i = rows ? rows[r] : r;
+                int32_t b = (int32_t)(bh / Hq), h = (int32_t)(bh % Hq);
+                int32_t kh = kv_map[h];
+                const int8_t* qp = q_i8 + (((int64_t)b * Hq + h) * S + i) * D;
+                const int8_t* Kh = k_i8 + ((int64_t)b * Hkv + kh) * S * D;
+                const double* Vh = V + ((int64_t)b * Hkv + kh) * S * D;
+                double dq = (double)q_scale[((int64_t)b * Hq + h) * nbq + i / bq];
+                const float* dk = k_scale + ((int64_t)b * Hkv + kh) * nbk;
+                double* o = out + t * D;
+                int32_t nvis = causal ? (i + 1 < S ? i + 1 : S) : S;
+                if (nvis <= 0) {
+                    for (int c = 0; c < D; ++c) o[c] = 0.0;
+                    if (lse) lse[t] = -INFINITY;
+                    continue;
+                }
+                double m = -INFINITY;
+                for (int32_t j = 0; j < nvis; ++j) {
+                    int64_t dot = 0;
+                    for (int c = 0; c < D; ++c) dot += (int64_t)qp[c] * (int64_t)Kh[(int64_t)j * D + c];
+                    s[j] = (double)dot * dq * (double)dk[j / bk] * sm_scale;
+                    if (s[j] > m) m = s[j];
+                }
+                double l = 0.0;
+                for (int c = 0; c < D; ++c) acc[c] = 0.0;
+                for (int32_t j = 0; j < nvis; ++j) {
+                    double p = exp(s[j] - m);
+                    double pr = oracle_round_to_half(p);
+                    l += l_from_rounded ? pr : p;
+                    for (int c = 0; c < D; ++c) acc[c] += pr * Vh[(int64_t)j * D + c];
+                }
+                for (int c = 0; c < D; ++c) o[c] = acc[c] / l;
+                if (lse) lse[t] = m + log(l);
+            }
+        }
+        free(s); free(acc);
+    }
+    free(V);
+    return status;
+}
+
+int oracle_max_threads(void) { return omp_get_max_threads(); }
