@@ -1,0 +1,200 @@
+"""MI355X-native 8-bit (SageAttention-form) attention forward.
+
+Thin Python binding over libattn.so (include/attn.h): every function below
+only checks and marshals arguments (device pointers, sizes, the current HIP
+stream) and calls the C ABI of the same name; all arithmetic runs in the HIP
+kernels.  torch provides device memory and streams.
+
+    attn_quantize_qk -> quantize_qk     K smoothing + per-block INT8 Q/K
+    attn_fwd_int8    -> fwd_int8        INT8 QK^T, FP16 PV, online softmax
+    attn_fwd_fp16    -> fwd_fp16        exact FP16 FlashAttention-style forward
+    attn_debug_qk_int32 -> debug_qk_int32   the INT32 score tiles (test hook)
+    sageattn(q, k, v, is_causal, scale)     one-call scaled_dot_product_attention replacement
+
+Sources: SageAttention article ("又快又准，即插即用！清华8比特量化Attention…"),
+技术方案 and its plug-and-play example; "注意力即一切：从 MHA 到 GQA" §2.2-§5.1.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _native
+from ._native import AttnShape, lib
+
+__all__ = [
+    "AttnError", "quant_blocks", "quantize_workspace_bytes", "quantize_qk", "fwd_int8",
+    "fwd_fp16", "debug_qk_int32", "sageattn", "status_string", "AttnShape", "lib",
+]
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+        self.status = status
+
+
+def status_string(status: int) -> str:
+    return lib().attn_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != _native.ATTN_OK:
+        raise AttnError(status, what)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t: torch.Tensor, dtype, name: str):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _shape(q: torch.Tensor, k: torch.Tensor) -> AttnShape:
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [batch, heads, seq, head_dim]")
+    B, Hq, S, D = q.shape
+    if k.shape[0] != B or k.shape[2] != S or k.shape[3] != D:
+        raise ValueError(f"k shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    return AttnShape(B, Hq, k.shape[1], S, D)
+
+
+def _map_arg(kv_head_map):
+    if kv_head_map is None:
+        return None, None
+    arr = (ctypes.c_int32 * len(kv_head_map))(*[int(x) for x in kv_head_map])
+    return arr, ctypes.cast(arr, ctypes.c_void_p)
+
+
+def quant_blocks():
+    bq, bk = ctypes.c_int32(), ctypes.c_int32()
+    lib().attn_quant_blocks(ctypes.byref(bq), ctypes.byref(bk))
+    return bq.value, bk.value
+
+
+def quantize_workspace_bytes(shape: AttnShape) -> int:
+    return int(lib().attn_quantize_workspace_bytes(ctypes.byref(shape)))
+
+
+def quantize_qk(q: torch.Tensor, k: torch.Tensor, *, out: Optional[dict] = None,
+                workspace: Optional[torch.Tensor] = None, with_mean: bool = True, stream=None):
+    """K smoothing + per-block INT8 quantisation.  Returns a dict with q_i8,
+    q_scale, k_i8, k_scale, k_mean (None unless with_mean) and workspace."""
+    _dev(q, torch.float16, "q")
+    _dev(k, torch.float16, "k")
+    sh = _shape(q, k)
+    bq, bk = quant_blocks()
+    B, Hq, Hkv, S, D = sh.batch, sh.heads_q, sh.heads_kv, sh.seq, sh.head_dim
+    o = dict(out) if out is not None else {}
+    dev = q.device
+    if "q_i8" not in o:
+        o["q_i8"] = torch.empty((B, Hq, S, D), dtype=torch.int8, device=dev)
+        o["q_scale"] = torch.empty((B, Hq, -(-S // bq)), dtype=torch.float32, device=dev)
+        o["k_i8"] = torch.empty((B, Hkv, S, D), dtype=torch.int8, device=dev)
+        o["k_scale"] = torch.empty((B, Hkv, -(-S // bk)), dtype=torch.float32, device=dev)
+    if with_mean and o.get("k_mean") is None:
+        o["k_mean"] = torch.empty((B, Hkv, D), dtype=torch.float32, device=dev)
+    if not with_mean:
+        o["k_mean"] = None
+    nbytes = quantize_workspace_bytes(sh)
+    if nbytes == 0:
+        raise AttnError(_native.ATTN_EINVAL, "attn_quantize_workspace_bytes")
+    if workspace is None:
+        workspace = o.get("workspace")
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    o["workspace"] = workspace
+    _check(lib().attn_quantize_qk(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(o["q_i8"]),
+                                  _ptr(o["q_scale"]), _ptr(o["k_i8"]), _ptr(o["k_scale"]),
+                                  _ptr(o["k_mean"]), _ptr(workspace), _stream(stream)),
+           "attn_quantize_qk")
+    return o
+
+
+def fwd_int8(qz: dict, v: torch.Tensor, *, causal: bool = False, kv_head_map=None,
+             sm_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+             lse: Optional[torch.Tensor] = None, return_lse: bool = False, stream=None):
+    """8-bit attention forward on the output of quantize_qk."""
+    q_i8 = _dev(qz["q_i8"], torch.int8, "q_i8")
+    k_i8 = _dev(qz["k_i8"], torch.int8, "k_i8")
+    qs = _dev(qz["q_scale"], torch.float32, "q_scale")
+    ks = _dev(qz["k_scale"], torch.float32, "k_scale")
+    _dev(v, torch.float16, "v")
+    sh = _shape(q_i8, k_i8)
+    if tuple(v.shape) != tuple(k_i8.shape):
+        raise ValueError("v must have the shape of k")
+    if out is None:
+        out = torch.empty(q_i8.shape, dtype=torch.float16, device=v.device)
+    _dev(out, torch.float16, "out")
+    if return_lse and lse is None:
+        lse = torch.empty(q_i8.shape[:3], dtype=torch.float32, device=v.device)
+    _keep, mp = _map_arg(kv_head_map)
+    _check(lib().attn_fwd_int8(ctypes.byref(sh), _ptr(q_i8), _ptr(qs), _ptr(k_i8), _ptr(ks),
+                               _ptr(v), _ptr(out), _ptr(lse), mp, int(bool(causal)),
+                               float(sm_scale or 0.0), _stream(stream)), "attn_fwd_int8")
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def fwd_fp16(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
+             kv_head_map=None, sm_scale: Optional[float] = None,
+             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+             return_lse: bool = False, stream=None):
+    """Exact FP16 attention forward (FlashAttention-style baseline)."""
+    _dev(q, torch.float16, "q")
+    _dev(k, torch.float16, "k")
+    _dev(v, torch.float16, "v")
+    sh = _shape(q, k)
+    if tuple(v.shape) != tuple(k.shape):
+        raise ValueError("v must have the shape of k")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, torch.float16, "out")
+    if return_lse and lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    _keep, mp = _map_arg(kv_head_map)
+    _check(lib().attn_fwd_fp16(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                               mp, int(bool(causal)), float(sm_scale or 0.0), _stream(stream)),
+           "attn_fwd_fp16")
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def debug_qk_int32(q_i8: torch.Tensor, k_i8: torch.Tensor, *, causal: bool = False,
+                   kv_head_map=None, tile_lo: int = 0, tile_hi: int = 0, fill: int = 0,
+                   stream=None) -> torch.Tensor:
+    """INT32 score rows of query tiles tile_lo..tile_hi: [B, Hq, ntiles*BQ, S];
+    masked entries and rows beyond S keep `fill`."""
+    _dev(q_i8, torch.int8, "q_i8")
+    _dev(k_i8, torch.int8, "k_i8")
+    sh = _shape(q_i8, k_i8)
+    bq, _ = quant_blocks()
+    rows = (tile_hi - tile_lo + 1) * bq
+    s_out = torch.full((sh.batch, sh.heads_q, max(rows, 1), sh.seq), fill, dtype=torch.int32,
+                       device=q_i8.device)
+    _keep, mp = _map_arg(kv_head_map)
+    _check(lib().attn_debug_qk_int32(ctypes.byref(sh), _ptr(q_i8), _ptr(k_i8), mp,
+                                     int(bool(causal)), int(tile_lo), int(tile_hi), _ptr(s_out),
+                                     _stream(stream)), "attn_debug_qk_int32")
+    return s_out
+
+
+def sageattn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: bool = False,
+             scale: Optional[float] = None, kv_head_map=None) -> torch.Tensor:
+    """Drop-in for torch's scaled_dot_product_attention on fp16 [B, H, S, D]
+    tensors (the SageAttention article's plug-and-play use): smoothing and
+    INT8 quantisation of Q/K, then the 8-bit fused forward."""
+    qz = quantize_qk(q.contiguous(), k.contiguous(), with_mean=False)
+    return fwd_int8(qz, v.contiguous(), causal=is_causal, kv_head_map=kv_head_map, sm_scale=scale)

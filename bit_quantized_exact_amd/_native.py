@@ -1,0 +1,63 @@
+"""ctypes loader of libattn.so (the C ABI declared in include/attn.h).
+
+torch is imported first on purpose: its HIP runtime then satisfies the
+library's libamdhip64 dependency, so both share one runtime, one device
+context and the same streams.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # noqa: F401  (must load before libattn.so, see above)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn.so")
+
+ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_ELAUNCH, ATTN_ERANGE = 0, -1, -2, -3, -4
+ATTN_MAX_HEADS = 256
+ATTN_MAX_SEQ = 1 << 22
+
+EXPORTED = (
+    "attn_quant_blocks", "attn_quantize_workspace_bytes", "attn_quantize_qk",
+    "attn_fwd_int8", "attn_fwd_fp16", "attn_debug_qk_int32", "attn_status_string",
+)
+
+
+class AttnShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads_q", ctypes.c_int32),
+                ("heads_kv", ctypes.c_int32), ("seq", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libattn.so; raise if it has not been built (there is no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m bit_quantized_exact_amd.build`; "
+            "this package has no non-HIP fallback")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+    SP = ctypes.POINTER(AttnShape)
+    L.attn_quant_blocks.argtypes = [ctypes.POINTER(I32), ctypes.POINTER(I32)]
+    L.attn_quant_blocks.restype = ctypes.c_int
+    L.attn_quantize_workspace_bytes.argtypes = [SP]
+    L.attn_quantize_workspace_bytes.restype = ctypes.c_size_t
+    L.attn_quantize_qk.argtypes = [SP, P, P, P, P, P, P, P, P, P]
+    L.attn_quantize_qk.restype = ctypes.c_int
+    L.attn_fwd_int8.argtypes = [SP, P, P, P, P, P, P, P, P, ctypes.c_int, F32, P]
+    L.attn_fwd_int8.restype = ctypes.c_int
+    L.attn_fwd_fp16.argtypes = [SP, P, P, P, P, P, P, ctypes.c_int, F32, P]
+    L.attn_fwd_fp16.restype = ctypes.c_int
+    L.attn_debug_qk_int32.argtypes = [SP, P, P, P, ctypes.c_int, I32, I32, P, P]
+    L.attn_debug_qk_int32.restype = ctypes.c_int
+    L.attn_status_string.argtypes = [ctypes.c_int]
+    L.attn_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L

@@ -1,0 +1,189 @@
+// C ABI of libattn.so: argument validation, launch geometry and dispatch.
+//
+// Validation is plain host code that runs before any HIP call, so every
+// rejected argument is observable without a GPU.  The library allocates
+// nothing: the caller passes every buffer, including the quantisation
+// workspace.
+#include "attn_internal.h"
+
+#include <cmath>
+#include <cstring>
+
+namespace attn {
+namespace {
+
+constexpr double kLog2e = 1.4426950408889634;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_shape(const attn_shape* s) {
+    if (!s) return ATTN_EINVAL;
+    if (s->batch <= 0 || s->heads_q <= 0 || s->heads_kv <= 0 || s->seq <= 0 || s->head_dim <= 0)
+        return ATTN_EINVAL;
+    if (s->head_dim != 64 && s->head_dim != 128) return ATTN_EUNSUPPORTED;
+    if (s->heads_q > ATTN_MAX_HEADS || s->heads_kv > ATTN_MAX_HEADS) return ATTN_EUNSUPPORTED;
+    if (s->seq > ATTN_MAX_SEQ) return ATTN_EUNSUPPORTED;
+    // one workgroup per (batch, q-head, 128-row tile) must fit a 1-D grid
+    const long long blocks = static_cast<long long>(s->batch) * s->heads_q * ceil_div(s->seq, kBM);
+    if (blocks > 0x7fffffffLL) return ATTN_EUNSUPPORTED;
+    // the quantisation grids put batch*heads_kv (and batch) in grid dimension y/z
+    if (static_cast<long long>(s->batch) * s->heads_kv > 65535LL) return ATTN_EUNSUPPORTED;
+    return ATTN_OK;
+}
+
+// Builds the q-head -> kv-head map and the launch order of q-heads (stable
+// sort by kv-head, so heads that share K/V are launched next to each other).
+int build_map(const attn_shape& s, const int32_t* user_map, FwdParams* p) {
+    if (!user_map) {
+        if (s.heads_q % s.heads_kv != 0) return ATTN_EINVAL;
+        const int grp = s.heads_q / s.heads_kv;
+        for (int h = 0; h < s.heads_q; ++h) p->kvmap[h] = static_cast<uint8_t>(h / grp);
+    } else {
+        for (int h = 0; h < s.heads_q; ++h) {
+            if (user_map[h] < 0 || user_map[h] >= s.heads_kv) return ATTN_ERANGE;
+            p->kvmap[h] = static_cast<uint8_t>(user_map[h]);
+        }
+    }
+    int n = 0;
+    for (int k = 0; k < s.heads_kv; ++k)
+        for (int h = 0; h < s.heads_q; ++h)
+            if (p->kvmap[h] == k) p->horder[n++] = static_cast<uint8_t>(h);
+    return ATTN_OK;
+}
+
+int check_scale(float sm_scale, int head_dim, float* scale_log2) {
+    if (std::isnan(sm_scale) || std::isinf(sm_scale)) return ATTN_EINVAL;
+    const double sc = sm_scale > 0.0f ? static_cast<double>(sm_scale) : 1.0 / std::sqrt(static_cast<double>(head_dim));
+    *scale_log2 = static_cast<float>(sc * kLog2e);
+    return ATTN_OK;
+}
+
+void fill_common(const attn_shape& s, FwdParams* p) {
+    p->B = s.batch;
+    p->Hq = s.heads_q;
+    p->Hkv = s.heads_kv;
+    p->S = s.seq;
+    p->nqt = ceil_div(s.seq, kBM);
+    p->nqblk = ceil_div(s.seq, kBQ);
+    p->nkblk = ceil_div(s.seq, kBK);
+    p->tile_lo = 0;
+    p->ntiles = p->nqt;
+}
+
+}  // namespace
+}  // namespace attn
+
+using namespace attn;
+
+extern "C" {
+
+int attn_quant_blocks(int32_t* bq, int32_t* bk) {
+    if (bq) *bq = kBQ;
+    if (bk) *bk = kBK;
+    return ATTN_OK;
+}
+
+size_t attn_quantize_workspace_bytes(const attn_shape* shape) {
+    if (check_shape(shape) != ATTN_OK) return 0;
+    return quant_workspace_layout(*shape, nullptr, nullptr);
+}
+
+int attn_quantize_qk(const attn_shape* shape, const void* q_f16, const void* k_f16, int8_t* q_i8,
+                     float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean, void* workspace,
+                     void* stream) {
+    int st = check_shape(shape);
+    if (st != ATTN_OK) return st;
+    if (!q_f16 || !k_f16 || !q_i8 || !q_scale || !k_i8 || !k_scale || !workspace) return ATTN_EINVAL;
+    if (!aligned(q_f16, 16) || !aligned(k_f16, 16) || !aligned(q_i8, 16) || !aligned(k_i8, 16) ||
+        !aligned(workspace, 16) || !aligned(q_scale, 4) || !aligned(k_scale, 4) ||
+        (k_mean && !aligned(k_mean, 4)))
+        return ATTN_EINVAL;
+    size_t mean_off = 0;
+    QuantWorkspace ws;
+    quant_workspace_layout(*shape, &mean_off, &ws.nchunk);
+    ws.partial = static_cast<long long*>(workspace);
+    ws.mean = reinterpret_cast<float*>(static_cast<char*>(workspace) + mean_off);
+    return launch_quantize(*shape, q_f16, k_f16, q_i8, q_scale, k_i8, k_scale, k_mean, ws,
+                           static_cast<hipStream_t>(stream));
+}
+
+int attn_fwd_int8(const attn_shape* shape, const int8_t* q_i8, const float* q_scale,
+                  const int8_t* k_i8, const float* k_scale, const void* v_f16, void* o_f16,
+                  float* lse, const int32_t* kv_head_map, int causal, float sm_scale,
+                  void* stream) {
+    int st = check_shape(shape);
+    if (st != ATTN_OK) return st;
+    if (!q_i8 || !q_scale || !k_i8 || !k_scale || !v_f16 || !o_f16) return ATTN_EINVAL;
+    if (!aligned(q_i8, 16) || !aligned(k_i8, 16) || !aligned(v_f16, 16) || !aligned(o_f16, 16) ||
+        !aligned(q_scale, 4) || !aligned(k_scale, 4) || (lse && !aligned(lse, 4)))
+        return ATTN_EINVAL;
+    FwdParams p;
+    std::memset(&p, 0, sizeof(p));
+    if ((st = build_map(*shape, kv_head_map, &p)) != ATTN_OK) return st;
+    if ((st = check_scale(sm_scale, shape->head_dim, &p.scale_log2)) != ATTN_OK) return st;
+    fill_common(*shape, &p);
+    p.q = q_i8;
+    p.k = k_i8;
+    p.v = v_f16;
+    p.o = o_f16;
+    p.lse = lse;
+    p.q_scale = q_scale;
+    p.k_scale = k_scale;
+    return launch_fwd(FwdKind::kInt8, shape->head_dim, causal != 0, p, static_cast<hipStream_t>(stream));
+}
+
+int attn_fwd_fp16(const attn_shape* shape, const void* q_f16, const void* k_f16, const void* v_f16,
+                  void* o_f16, float* lse, const int32_t* kv_head_map, int causal, float sm_scale,
+                  void* stream) {
+    int st = check_shape(shape);
+    if (st != ATTN_OK) return st;
+    if (!q_f16 || !k_f16 || !v_f16 || !o_f16) return ATTN_EINVAL;
+    if (!aligned(q_f16, 16) || !aligned(k_f16, 16) || !aligned(v_f16, 16) || !aligned(o_f16, 16) ||
+        (lse && !aligned(lse, 4)))
+        return ATTN_EINVAL;
+    FwdParams p;
+    std::memset(&p, 0, sizeof(p));
+    if ((st = build_map(*shape, kv_head_map, &p)) != ATTN_OK) return st;
+    if ((st = check_scale(sm_scale, shape->head_dim, &p.scale_log2)) != ATTN_OK) return st;
+    fill_common(*shape, &p);
+    p.q = q_f16;
+    p.k = k_f16;
+    p.v = v_f16;
+    p.o = o_f16;
+    p.lse = lse;
+    return launch_fwd(FwdKind::kFp16, shape->head_dim, causal != 0, p, static_cast<hipStream_t>(stream));
+}
+
+int attn_debug_qk_int32(const attn_shape* shape, const int8_t* q_i8, const int8_t* k_i8,
+                        const int32_t* kv_head_map, int causal, int32_t q_tile_lo,
+                        int32_t q_tile_hi, int32_t* s_out, void* stream) {
+    int st = check_shape(shape);
+    if (st != ATTN_OK) return st;
+    if (!q_i8 || !k_i8 || !s_out) return ATTN_EINVAL;
+    if (!aligned(q_i8, 16) || !aligned(k_i8, 16) || !aligned(s_out, 4)) return ATTN_EINVAL;
+    const int nqt = ceil_div(shape->seq, kBM);
+    if (q_tile_lo < 0 || q_tile_hi < q_tile_lo || q_tile_hi >= nqt) return ATTN_EINVAL;
+    FwdParams p;
+    std::memset(&p, 0, sizeof(p));
+    if ((st = build_map(*shape, kv_head_map, &p)) != ATTN_OK) return st;
+    fill_common(*shape, &p);
+    p.q = q_i8;
+    p.k = k_i8;
+    p.s_out = s_out;
+    p.tile_lo = q_tile_lo;
+    p.ntiles = q_tile_hi - q_tile_lo + 1;
+    return launch_fwd(FwdKind::kDumpInt8, shape->head_dim, causal != 0, p, static_cast<hipStream_t>(stream));
+}
+
+const char* attn_status_string(int status) {
+    switch (status) {
+        case ATTN_OK: return "ok";
+        case ATTN_EINVAL: return "invalid argument";
+        case ATTN_EUNSUPPORTED: return "unsupported shape";
+        case ATTN_ELAUNCH: return "kernel launch failed";
+        case ATTN_ERANGE: return "kv_head_map entry out of range";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,64 @@
+// Internal declarations shared by the host API and the kernel translation
+// units of libattn.so.  Not part of the public ABI (that is include/attn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+#include "attn.h"
+
+namespace attn {
+
+// Quantisation blocks: rows of Q per scale, rows of (smoothed) K per scale.
+constexpr int kBQ = 128;
+constexpr int kBK = 64;
+
+// Forward tiling: a workgroup owns BM query rows (4 waves x 32 rows) and walks
+// the keys BN at a time.  BM == kBQ and BN == kBK, so one Q scale covers a
+// workgroup and one K scale covers a key tile.
+constexpr int kBM = 128;
+constexpr int kBN = 64;
+constexpr int kFwdThreads = 256;
+
+// K column sums: tokens per partial-sum chunk.
+constexpr int kSumChunk = 256;
+
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+struct QuantWorkspace {
+    long long* partial;   // [B*Hkv, nchunk, D] exact channel sums, units of 2^-24
+    float* mean;          // [B*Hkv, D]
+    int nchunk;
+};
+
+// Offsets of the workspace pieces for a shape (256-byte aligned pieces).
+size_t quant_workspace_layout(const attn_shape& s, size_t* mean_offset, int* nchunk);
+
+int launch_quantize(const attn_shape& s, const void* q, const void* k, int8_t* q_i8,
+                    float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
+                    const QuantWorkspace& ws, hipStream_t st);
+
+struct FwdParams {
+    const void* q;        // fp16 or int8 [B,Hq,S,D]
+    const void* k;        // fp16 or int8 [B,Hkv,S,D]
+    const void* v;        // fp16 [B,Hkv,S,D]
+    void* o;              // fp16 [B,Hq,S,D]
+    float* lse;           // fp32 [B,Hq,S] or null
+    const float* q_scale; // int8 path: [B,Hq,nqblk]
+    const float* k_scale; // int8 path: [B,Hkv,nkblk]
+    int32_t* s_out;       // score dump: [B,Hq,ntiles*BM,S]
+    int B, Hq, Hkv, S;
+    int nqt;              // query tiles in the sequence
+    int nqblk, nkblk;     // scale blocks per (b, head)
+    int tile_lo, ntiles;  // query tiles handled by this launch
+    float scale_log2;     // sm_scale * log2(e)
+    uint8_t kvmap[ATTN_MAX_HEADS];   // q-head -> kv-head
+    uint8_t horder[ATTN_MAX_HEADS];  // q-heads ordered by kv-head (launch order)
+};
+
+enum class FwdKind { kFp16, kInt8, kDumpInt8 };
+
+int launch_fwd(FwdKind kind, int head_dim, bool causal, const FwdParams& p, hipStream_t st);
+
+}  // namespace attn

@@ -1,0 +1,230 @@
+// K smoothing and per-block INT8 quantisation of Q and K for gfx950.
+//
+// SageAttention article ("又快又准，即插即用！清华8比特量化Attention…"), section
+// 技术方案: K <- K - mean(K) removes K's channel outliers and leaves softmax
+// unchanged; Q and K are then quantised to INT8 with one scale per
+// FlashAttention-sized block.  The pages print neither the scale formula nor
+// the rounding; this file implements the symmetric absmax reading
+// (delta = max|x| / 127, q = rint(x * (127 / max|x|)) saturated to +-127,
+// ties to even) with the mean taken per channel over all tokens.
+//
+// Every result here is bit-exact by construction and independent of launch
+// order and reduction order:
+//   * the channel sum is accumulated exactly in int64 fixed point (every fp16
+//     value is an integer multiple of 2^-24, below 2^40 in those units), so
+//     any summation order gives the same integer;
+//   * maxima are exact;
+//   * the remaining fp32 operations (subtract, two correctly rounded
+//     divisions, one product, rint) are single IEEE operations.  This file is
+//     compiled with -ffp-contract=off so that no product is fused.
+//
+// All four kernels stream HBM: each reads its inputs once (K twice: sums, then
+// quantisation) with 16-byte loads and writes int8 with 8-byte stores.
+#include "attn_internal.h"
+
+#include <cfloat>
+
+namespace attn {
+namespace {
+
+typedef int i4x __attribute__((ext_vector_type(4)));
+typedef int i2x __attribute__((ext_vector_type(2)));
+
+// fp16 bit pattern -> exact value in units of 2^-24 (finite inputs).
+__device__ __forceinline__ long long half_to_fixed(unsigned h) {
+    const int e = (h >> 10) & 31;
+    const int f = h & 1023;
+    const long long mag = e ? (static_cast<long long>(1024 + f) << (e - 1)) : f;
+    return (h & 0x8000u) ? -mag : mag;
+}
+
+__device__ __forceinline__ float half_bits_to_float(unsigned h) {
+    _Float16 x;
+    const unsigned short s = static_cast<unsigned short>(h);
+    __builtin_memcpy(&x, &s, 2);
+    return static_cast<float>(x);
+}
+
+// Per (b, kv-head, chunk of kSumChunk tokens): exact column sums of K.
+// Thread t owns one 16-byte column chunk (8 channels) and a strided set of
+// rows; the row groups are then combined through LDS (integer adds).
+template <int D>
+__global__ __launch_bounds__(256) void k_colsum_kernel(const uint16_t* __restrict__ k, int S,
+                                                       int nchunk,
+                                                       long long* __restrict__ partial) {
+    constexpr int CPR = D / 8;          // 16-byte chunks per row
+    constexpr int RG = 256 / CPR;       // row groups
+    __shared__ long long red[RG][D];
+    const int t = threadIdx.x;
+    const int cc = t % CPR, rg = t / CPR;
+    const int chunk = blockIdx.x;
+    const size_t bk = blockIdx.y;
+    const uint16_t* base = k + bk * static_cast<size_t>(S) * D;
+    long long acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    const int r0 = chunk * kSumChunk;
+    for (int r = r0 + rg; r < r0 + kSumChunk && r < S; r += RG) {
+        const i4x v = *reinterpret_cast<const i4x*>(base + static_cast<size_t>(r) * D + cc * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const unsigned w = static_cast<unsigned>(v[e]);
+            acc[2 * e] += half_to_fixed(w & 0xffffu);
+            acc[2 * e + 1] += half_to_fixed(w >> 16);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[rg][cc * 8 + e] = acc[e];
+    __syncthreads();
+    if (t < D) {
+        long long s = 0;
+        for (int g = 0; g < RG; ++g) s += red[g][t];
+        partial[(bk * nchunk + chunk) * D + t] = s;
+    }
+}
+
+// Per (b, kv-head): total over chunks, mu = fp32(fp64(sum) / S).
+template <int D>
+__global__ __launch_bounds__(D) void k_mean_kernel(const long long* __restrict__ partial, int S,
+                                                   int nchunk, float* __restrict__ mean,
+                                                   float* __restrict__ mean_out) {
+    const size_t bk = blockIdx.x;
+    const int c = threadIdx.x;
+    long long s = 0;
+    for (int i = 0; i < nchunk; ++i) s += partial[(bk * nchunk + i) * D + c];
+    // (double)s is exact below 2^53 and correctly rounded above; the 2^-24
+    // scaling is exact; the division and the narrowing are IEEE operations.
+    const double total = __builtin_ldexp(static_cast<double>(s), -24);
+    const float mu = static_cast<float>(total / static_cast<double>(S));
+    mean[bk * D + c] = mu;
+    if (mean_out) mean_out[bk * D + c] = mu;
+}
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[wave] = v;
+    __syncthreads();
+    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+__device__ __forceinline__ int quant_one(float x, float r) {
+    float t = __builtin_rintf(x * r);
+    t = fminf(fmaxf(t, -127.0f), 127.0f);
+    return static_cast<int>(t);
+}
+
+// One block of ROWS rows of one (b, head) matrix: absmax, scale, int8.
+// SMOOTH subtracts the channel mean first (K); Q is quantised as is.
+template <int D, int ROWS, bool SMOOTH>
+__global__ __launch_bounds__(256) void quant_block_kernel(const uint16_t* __restrict__ x,
+                                                          const float* __restrict__ mean,
+                                                          int8_t* __restrict__ q,
+                                                          float* __restrict__ scale, int H,
+                                                          int S, int nblk) {
+    constexpr int CPR = D / 8;
+    constexpr int CHUNKS = ROWS * CPR;
+    constexpr int PER = CHUNKS / 256;
+    static_assert(CHUNKS % 256 == 0, "chunks must split evenly");
+    __shared__ float red[4];
+    const int t = threadIdx.x;
+    const int cc = t % CPR;   // 256 % CPR == 0: the column chunk is fixed per thread
+    const int blk = blockIdx.x;
+    const size_t mat = static_cast<size_t>(blockIdx.z) * H + blockIdx.y;
+    const uint16_t* xb = x + mat * static_cast<size_t>(S) * D;
+    int8_t* qb = q + mat * static_cast<size_t>(S) * D;
+    const int r0 = blk * ROWS;
+
+    float mu[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mu[e] = SMOOTH ? mean[mat * D + cc * 8 + e] : 0.0f;
+
+    float v[PER][8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int row = r0 + (t + 256 * i) / CPR;
+        if (row < S) {
+            const i4x w = *reinterpret_cast<const i4x*>(xb + static_cast<size_t>(row) * D + cc * 8);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const unsigned u = static_cast<unsigned>(w[e]);
+                float lo = half_bits_to_float(u & 0xffffu);
+                float hi = half_bits_to_float(u >> 16);
+                if (SMOOTH) {
+                    lo = lo - mu[2 * e];
+                    hi = hi - mu[2 * e + 1];
+                }
+                v[i][2 * e] = lo;
+                v[i][2 * e + 1] = hi;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[i][e] = 0.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[i][e]));
+    }
+    const float a = block_max(amax, red);
+    const float r = (a == 0.0f) ? 0.0f : __fdiv_rn(127.0f, a);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int row = r0 + (t + 256 * i) / CPR;
+        if (row < S) {
+            unsigned packed[2] = {0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const unsigned b8 = static_cast<unsigned>(quant_one(v[i][e], r)) & 0xffu;
+                packed[e / 4] |= b8 << (8 * (e % 4));
+            }
+            i2x out;
+            out[0] = static_cast<int>(packed[0]);
+            out[1] = static_cast<int>(packed[1]);
+            *reinterpret_cast<i2x*>(qb + static_cast<size_t>(row) * D + cc * 8) = out;
+        }
+    }
+    if (t == 0) scale[mat * nblk + blk] = (a == 0.0f) ? 0.0f : __fdiv_rn(a, 127.0f);
+}
+
+template <int D>
+int launch_quantize_d(const attn_shape& s, const void* q, const void* k, int8_t* q_i8,
+                      float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
+                      const QuantWorkspace& ws, hipStream_t st) {
+    const int S = s.seq;
+    const int BH_kv = s.batch * s.heads_kv;
+    const uint16_t* kk = static_cast<const uint16_t*>(k);
+    const uint16_t* qq = static_cast<const uint16_t*>(q);
+    hipLaunchKernelGGL(k_colsum_kernel<D>, dim3(ws.nchunk, BH_kv), dim3(256), 0, st, kk, S,
+                       ws.nchunk, ws.partial);
+    hipLaunchKernelGGL(k_mean_kernel<D>, dim3(BH_kv), dim3(D), 0, st, ws.partial, S, ws.nchunk,
+                       ws.mean, k_mean);
+    const int nkb = ceil_div(S, kBK), nqb = ceil_div(S, kBQ);
+    hipLaunchKernelGGL((quant_block_kernel<D, kBK, true>), dim3(nkb, s.heads_kv, s.batch),
+                       dim3(256), 0, st, kk, ws.mean, k_i8, k_scale, s.heads_kv, S, nkb);
+    hipLaunchKernelGGL((quant_block_kernel<D, kBQ, false>), dim3(nqb, s.heads_q, s.batch),
+                       dim3(256), 0, st, qq, static_cast<const float*>(nullptr), q_i8, q_scale,
+                       s.heads_q, S, nqb);
+    return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ELAUNCH;
+}
+
+}  // namespace
+
+size_t quant_workspace_layout(const attn_shape& s, size_t* mean_offset, int* nchunk) {
+    const int nc = ceil_div(s.seq, kSumChunk);
+    const size_t bh = static_cast<size_t>(s.batch) * s.heads_kv;
+    const size_t part = bh * nc * s.head_dim * sizeof(long long);
+    const size_t off = (part + 255) & ~static_cast<size_t>(255);
+    const size_t total = off + bh * s.head_dim * sizeof(float);
+    if (mean_offset) *mean_offset = off;
+    if (nchunk) *nchunk = nc;
+    return (total + 255) & ~static_cast<size_t>(255);
+}
+
+int launch_quantize(const attn_shape& s, const void* q, const void* k, int8_t* q_i8,
+                    float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
+                    const QuantWorkspace& ws, hipStream_t st) {
+    if (s.head_dim == 64)
+        return launch_quantize_d<64>(s, q, k, q_i8, q_scale, k_i8, k_scale, k_mean, ws, st);
+    return launch_quantize_d<128>(s, q, k, q_i8, q_scale, k_i8, k_scale, k_mean, ws, st);
+}
+
+}  // namespace attn

@@ -1,0 +1,156 @@
+/*
+ * attn.h - C ABI of the MI355X (gfx950) 8-bit attention forward library
+ * (libattn.so).
+ *
+ * The library computes the attention forward pass O = softmax(Q K^T * scale) V
+ * in two forms:
+ *   - the 8-bit SageAttention form: K is smoothed by subtracting its
+ *     per-channel mean over tokens, Q and K are quantised per block to INT8,
+ *     Q K^T runs as an INT8 contraction with INT32 accumulation and is
+ *     dequantised with the block scales, and P V runs with P and V in FP16;
+ *   - an exact FP16 FlashAttention-style form (tiled, online softmax).
+ *
+ * Sources (web pages; cited by title and section):
+ *   [SA]       "又快又准，即插即用！清华8比特量化Attention，两倍加速于
+ *              FlashAttention2，各端到端任务均不掉点！" (SageAttention article,
+ *              17aitech reprint), section 技术方案 (technical approach) and its
+ *              plug-and-play example (a drop-in for scaled_dot_product_attention).
+ *   [MHA-GQA]  "注意力即一切：从 MHA 到 GQA" (bojinhu.xyz), §2.2 (the four steps),
+ *              §2.3 (causal mask), §4.1 (MQA), §5.1 (GQA), §8.2 (tiling and
+ *              online softmax).
+ *   [FA-guide] "FlashAttention" guide (aiunderstanding.org): tiling in on-chip
+ *              memory, online softmax, exactness.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Layout.  Q, O: [batch, heads_q, seq, head_dim]; K, V: [batch, heads_kv, seq,
+ *   head_dim]; all contiguous, row-major, head_dim innermost.  Q and K share
+ *   one sequence length.  head_dim must be 64 or 128.
+ * Memory.  Every tensor pointer is DEVICE memory owned by the caller, 16-byte
+ *   aligned.  The library allocates and frees nothing and keeps no mutable
+ *   global state; calls are thread-safe.  kv_head_map is a HOST pointer.
+ * Execution.  Every call enqueues its kernels on `stream` (a hipStream_t; NULL
+ *   means the null stream) and returns without synchronising.
+ * Errors.  Calls return a status code and never throw.  All argument checks run
+ *   on the host before any HIP call, so a rejected call touches no device
+ *   state.  A failed launch returns ATTN_ELAUNCH.  Input values must be finite;
+ *   results for inf/nan inputs are unspecified.
+ * GQA/MQA ([MHA-GQA] §4.1, §5.1).  Query head h reads K/V of kv-head map[h].
+ *   kv_head_map == NULL selects map[h] = h / (heads_q / heads_kv), which needs
+ *   heads_q % heads_kv == 0.  An explicit map has heads_q entries in
+ *   [0, heads_kv).  heads_q and heads_kv are at most ATTN_MAX_HEADS.
+ * Scale.  sm_scale <= 0 selects 1/sqrt(head_dim) ([MHA-GQA] §2.2).
+ * Causal ([MHA-GQA] §2.3).  causal != 0 gives key j weight 0 for query i when
+ *   j > i.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct attn_shape {
+    int32_t batch;
+    int32_t heads_q;
+    int32_t heads_kv;
+    int32_t seq;       /* 1 .. ATTN_MAX_SEQ */
+    int32_t head_dim;  /* 64 or 128 */
+} attn_shape;
+
+enum {
+    ATTN_OK = 0,
+    ATTN_EINVAL = -1,       /* null pointer, non-positive size, misalignment, bad argument */
+    ATTN_EUNSUPPORTED = -2, /* head_dim not 64/128, too many heads, sequence too long */
+    ATTN_ELAUNCH = -3,      /* a kernel launch failed */
+    ATTN_ERANGE = -4        /* kv_head_map entry outside [0, heads_kv) */
+};
+
+#define ATTN_MAX_HEADS 256
+#define ATTN_MAX_SEQ (1 << 22)
+
+/* Quantisation block sizes: rows per Q block (BQ) and per K block (BK).
+ * [SA] 技术方案 sets the granularity to the FlashAttention tile; the pages
+ * print no number, the library uses BQ = 128, BK = 64.  Either pointer may be
+ * NULL.  Returns ATTN_OK. */
+int attn_quant_blocks(int32_t* bq, int32_t* bk);
+
+/* Bytes of device workspace attn_quantize_qk needs for `shape` (the per-chunk
+ * exact channel sums of K and the fp32 channel means).  0 for an invalid
+ * shape. */
+size_t attn_quantize_workspace_bytes(const attn_shape* shape);
+
+/* K smoothing and per-block INT8 quantisation of Q and K ([SA] 技术方案).
+ *
+ * mean: mu[b,k,c] = fp32( fp64(sum_j K[b,k,j,c]) / S ), the sum over all S
+ *       tokens taken exactly (fp16 values are integer multiples of 2^-24),
+ *       rounded once to fp64, divided by S in fp64, rounded to fp32.  The mean
+ *       runs over all tokens also for causal attention: the shift q_i . mu is
+ *       constant along each score row, so softmax is unchanged.
+ * smooth: ks = fp32(K) - mu (one fp32 subtraction).  Q is not smoothed.
+ * quantise, per block X of BQ rows of one (b,h) of Q, or BK rows of one
+ *       (b,k) of ks (the last block of a sequence may be partial):
+ *       a = max|x|; a == 0 gives q = 0, delta = 0; otherwise r = 127/a and
+ *       delta = a/127 (fp32, correctly rounded), q = clamp(rint(x*r), -127, 127)
+ *       with x*r one fp32 product and rint ties-to-even.
+ *
+ * q_f16   in   fp16 [B,Hq,S,D]
+ * k_f16   in   fp16 [B,Hkv,S,D]
+ * q_i8    out  int8 [B,Hq,S,D]
+ * q_scale out  fp32 [B,Hq,ceil(S/BQ)]
+ * k_i8    out  int8 [B,Hkv,S,D]   (quantised smoothed K)
+ * k_scale out  fp32 [B,Hkv,ceil(S/BK)]
+ * k_mean  out  fp32 [B,Hkv,D] or NULL
+ * workspace    device scratch of attn_quantize_workspace_bytes(shape) bytes,
+ *              16-byte aligned; its contents on entry are ignored.
+ * Results are bit-exact and independent of launch order. */
+int attn_quantize_qk(const attn_shape* shape, const void* q_f16, const void* k_f16,
+                     int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
+                     float* k_mean, void* workspace, void* stream);
+
+/* 8-bit attention forward ([SA] 技术方案; tiling and online softmax per
+ * [FA-guide] and [MHA-GQA] §8.2).
+ *   S32[i,j] = sum_c q_i8[i,c] * k_i8[j,c]            (INT8 MFMA, exact INT32)
+ *   s[i,j]   = S32[i,j] * q_scale[i/BQ] * k_scale[j/BK] * sm_scale
+ *   P        = online softmax of s over the visible keys, rounded to fp16
+ *   O        = (P V) / rowsum   (FP16 MFMA, fp32 accumulation), stored fp16
+ * Inputs are the outputs of attn_quantize_qk plus V fp16 [B,Hkv,S,D].
+ * o_f16 out fp16 [B,Hq,S,D]; lse out fp32 [B,Hq,S] (natural-log
+ * log-sum-exp of s per row) or NULL. */
+int attn_fwd_int8(const attn_shape* shape, const int8_t* q_i8, const float* q_scale,
+                  const int8_t* k_i8, const float* k_scale, const void* v_f16,
+                  void* o_f16, float* lse, const int32_t* kv_head_map, int causal,
+                  float sm_scale, void* stream);
+
+/* Exact FP16 attention forward (the FlashAttention-style baseline,
+ * [FA-guide]: exact values, tiles in on-chip memory, online softmax).
+ *   s = (Q K^T) * sm_scale with FP16 MFMA and fp32 accumulation, online
+ *   softmax in fp32, P rounded to fp16 for P V (FP16 MFMA, fp32 accumulation),
+ *   O = (P V) / rowsum stored as fp16; lse as for attn_fwd_int8. */
+int attn_fwd_fp16(const attn_shape* shape, const void* q_f16, const void* k_f16,
+                  const void* v_f16, void* o_f16, float* lse,
+                  const int32_t* kv_head_map, int causal, float sm_scale, void* stream);
+
+/* Test hook: the INT32 score tiles of attn_fwd_int8, produced by the same
+ * tile code, written out instead of being consumed.  For every (b, h) and
+ * every query row i in q-tiles q_tile_lo..q_tile_hi (tiles of BQ rows,
+ * inclusive; 0 <= q_tile_lo <= q_tile_hi < ceil(S/BQ), else ATTN_EINVAL),
+ * writes S32[i, j] for every visible key
+ * j to s_out[b, h, i - q_tile_lo*BQ, j]; s_out is int32
+ * [B, Hq, (q_tile_hi - q_tile_lo + 1) * BQ, S].  Entries of masked keys
+ * (j > i when causal) and of rows beyond S are left untouched. */
+int attn_debug_qk_int32(const attn_shape* shape, const int8_t* q_i8, const int8_t* k_i8,
+                        const int32_t* kv_head_map, int causal, int32_t q_tile_lo,
+                        int32_t q_tile_hi, int32_t* s_out, void* stream);
+
+/* Static text for a status code. */
+const char* attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

@@ -1,0 +1,165 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol that
+include/attn.h declares, and rejects every invalid argument on the host,
+before any HIP call (each call below fails validation, so nothing launches)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_quantized_exact_amd as A
+from bit_quantized_exact_amd import _native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000          # 16-byte aligned, never dereferenced: validation fails first
+MISALIGNED = 0x10008
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "attn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == sorted(_native.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = A.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def test_quant_blocks_and_status_strings():
+    assert A.quant_blocks() == (128, 64)
+    L = A.lib()
+    assert L.attn_quant_blocks(None, None) == 0
+    for st in (0, -1, -2, -3, -4):
+        assert A.status_string(st) and A.status_string(st) != "unknown status"
+    assert A.status_string(7) == "unknown status"
+
+
+def _sh(B=1, Hq=4, Hkv=2, S=256, D=128):
+    return A.AttnShape(B, Hq, Hkv, S, D)
+
+
+def test_workspace_bytes():
+    n = A.quantize_workspace_bytes(_sh())
+    # partial sums (int64) for 1 chunk of 256 tokens, 2 kv-heads, 128 channels, plus the means
+    assert n >= 2 * 1 * 128 * 8 + 2 * 128 * 4 and n % 256 == 0
+    assert A.quantize_workspace_bytes(_sh(D=96)) == 0
+    assert A.lib().attn_quantize_workspace_bytes(None) == 0
+    big = A.quantize_workspace_bytes(_sh(B=2, Hkv=8, Hq=32, S=32768))
+    assert big >= 2 * 8 * 128 * 128 * 8
+
+
+def _fp16(L, sh, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, mp=None, causal=0, scale=0.0):
+    return L.attn_fwd_fp16(ctypes.byref(sh) if sh is not None else None, q, k, v, o, lse, mp,
+                           causal, scale, None)
+
+
+def _int8(L, sh, q=FAKE, qs=FAKE, k=FAKE, ks=FAKE, v=FAKE, o=FAKE, lse=None, mp=None, scale=0.0):
+    return L.attn_fwd_int8(ctypes.byref(sh) if sh is not None else None, q, qs, k, ks, v, o, lse,
+                           mp, 0, scale, None)
+
+
+def _quant(L, sh, q=FAKE, k=FAKE, qi=FAKE, qs=FAKE, ki=FAKE, ks=FAKE, mean=None, ws=FAKE):
+    return L.attn_quantize_qk(ctypes.byref(sh) if sh is not None else None, q, k, qi, qs, ki, ks,
+                              mean, ws, None)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("batch", 0, -1), ("heads_q", -1, -1), ("heads_kv", 0, -1), ("seq", 0, -1),
+    ("head_dim", 0, -1), ("head_dim", 96, -2), ("head_dim", 256, -2),
+    ("heads_q", 257, -2), ("seq", (1 << 22) + 1, -2)])
+def test_shape_validation(field, value, code):
+    L = A.lib()
+    sh = _sh()
+    setattr(sh, field, value)
+    assert _fp16(L, sh) == code
+    assert _int8(L, sh) == code
+    assert _quant(L, sh) == code
+
+
+def test_null_shape():
+    L = A.lib()
+    assert _fp16(L, None) == -1
+    assert _int8(L, None) == -1
+    assert _quant(L, None) == -1
+    assert L.attn_debug_qk_int32(None, FAKE, FAKE, None, 0, 0, 0, FAKE, None) == -1
+
+
+@pytest.mark.parametrize("arg", ["q", "k", "v", "o"])
+def test_fp16_null_and_misaligned(arg):
+    L = A.lib()
+    assert _fp16(L, _sh(), **{arg: None}) == -1
+    assert _fp16(L, _sh(), **{arg: MISALIGNED}) == -1
+
+
+def test_fp16_lse_alignment():
+    assert _fp16(A.lib(), _sh(), lse=FAKE + 2) == -1
+
+
+@pytest.mark.parametrize("arg", ["q", "qs", "k", "ks", "v", "o"])
+def test_int8_null(arg):
+    assert _int8(A.lib(), _sh(), **{arg: None}) == -1
+
+
+@pytest.mark.parametrize("arg", ["q", "k", "qi", "qs", "ki", "ks", "ws"])
+def test_quant_null(arg):
+    assert _quant(A.lib(), _sh(), **{arg: None}) == -1
+
+
+def test_quant_misaligned():
+    L = A.lib()
+    assert _quant(L, _sh(), q=MISALIGNED) == -1
+    assert _quant(L, _sh(), ws=MISALIGNED) == -1
+    assert _quant(L, _sh(), qs=FAKE + 2) == -1
+
+
+def test_group_divisibility_without_map():
+    L = A.lib()
+    sh = _sh(Hq=6, Hkv=4)
+    assert _fp16(L, sh) == -1
+    assert _int8(L, sh) == -1
+
+
+def test_map_entries_out_of_range():
+    L = A.lib()
+    sh = _sh(Hq=4, Hkv=2)
+    # make the call fail at the map check: map validated before launch, and a
+    # NaN scale afterwards would also fail; use both orders to be sure nothing launches
+    bad = (ctypes.c_int32 * 4)(0, 1, 2, 0)
+    assert _fp16(L, sh, mp=ctypes.cast(bad, ctypes.c_void_p)) == -4
+    neg = (ctypes.c_int32 * 4)(0, -1, 1, 0)
+    assert _int8(L, sh, mp=ctypes.cast(neg, ctypes.c_void_p)) == -4
+
+
+def test_nan_scale_rejected():
+    L = A.lib()
+    assert _fp16(L, _sh(), scale=float("nan")) == -1
+    assert _int8(L, _sh(), scale=float("inf")) == -1
+
+
+@pytest.mark.parametrize("lo,hi", [(-1, 0), (1, 0), (0, 2), (2, 2)])
+def test_debug_tile_range(lo, hi):
+    L = A.lib()
+    sh = _sh(S=256)    # two query tiles
+    assert L.attn_debug_qk_int32(ctypes.byref(sh), FAKE, FAKE, None, 0, lo, hi, FAKE, None) == -1
+
+
+def test_debug_null_and_alignment():
+    L = A.lib()
+    sh = _sh()
+    assert L.attn_debug_qk_int32(ctypes.byref(sh), None, FAKE, None, 0, 0, 0, FAKE, None) == -1
+    assert L.attn_debug_qk_int32(ctypes.byref(sh), FAKE, FAKE, None, 0, 0, 0, FAKE + 2, None) == -1
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 2, 16, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        A.fwd_fp16(q, q, q)
+    with pytest.raises(ValueError):
+        A.quantize_qk(q, q)

@@ -1,0 +1,263 @@
+"""GPU parity of the fused forward kernels against the CPU oracle.
+
+* INT32 score tiles (attn_debug_qk_int32, same tile code as attn_fwd_int8):
+  bit-exact against the oracle's integer scores.
+* FP16 path (attn_fwd_fp16): max-abs <= 2e-3 against fp64 exact attention.
+* INT8 path (attn_fwd_int8): cosine >= 0.999 and relative L1 <= 0.02 against
+  fp64 exact attention; max-abs <= 2e-3 against the oracle's quantised model
+  (which separates kernel error from quantisation error).
+* Invariants from the pages: a constant V gives that constant, causal row 0
+  gives V_0, GQA/MQA share K/V per group; plus run-to-run determinism.
+
+Small cases cover every tail class (S = 1..17, 63-65, 127-129, 1000), both
+head dims, MHA/GQA/MQA and an explicit non-contiguous map; the workload
+cases run the full-size launch and compare sampled rows."""
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_exact_amd as A
+from bit_quantized_exact_amd.inputs import WORKLOADS, make_qkv, sample_rows
+from oracle import oracle as O
+
+from _util import (FP16_MAX_ABS, INT8_COS_MIN, INT8_REL_L1_MAX, INT8_VS_MODEL_MAX_ABS, case,
+                   cos_rel_l1, dev, host, small_workload)
+
+pytestmark = pytest.mark.gpu
+
+TAILS = list(range(1, 18)) + [63, 64, 65, 127, 128, 129, 1000]
+
+
+def _fp16_check(w, q, k, v, rows=None, kv_map=None):
+    case(f"fwd_fp16 {w.name} S={w.seq} D={w.head_dim} causal={w.causal} map={kv_map}")
+    out = A.fwd_fp16(dev(q), dev(k), dev(v), causal=w.causal, kv_head_map=kv_map)
+    torch.cuda.synchronize()
+    got = host(out).astype(np.float64)
+    if rows is not None:
+        got = got[:, :, rows]
+    ref = O.attention(q, k, v, causal=w.causal, kv_map=kv_map, rows=rows)
+    err = np.abs(got - ref).max()
+    assert err <= FP16_MAX_ABS, f"max-abs {err}"
+    return err
+
+
+def _int8_check(w, q, k, v, rows=None, kv_map=None):
+    case(f"fwd_int8 {w.name} S={w.seq} D={w.head_dim} causal={w.causal} map={kv_map}")
+    qz = A.quantize_qk(dev(q), dev(k))
+    out = A.fwd_int8(qz, dev(v), causal=w.causal, kv_head_map=kv_map)
+    torch.cuda.synchronize()
+    got = host(out).astype(np.float64)
+    if rows is not None:
+        got = got[:, :, rows]
+    exact = O.attention(q, k, v, causal=w.causal, kv_map=kv_map, rows=rows)
+    cos, rel = cos_rel_l1(got, exact)
+    assert cos >= INT8_COS_MIN and rel <= INT8_REL_L1_MAX, (cos, rel)
+    qz_h = {key: host(qz[key]) for key in ("q_i8", "q_scale", "k_i8", "k_scale")}
+    model = O.quant_attention(qz_h, v, causal=w.causal, kv_map=kv_map, rows=rows)
+    err = np.abs(got - model).max()
+    assert err <= INT8_VS_MODEL_MAX_ABS, f"max-abs vs quantised model {err}"
+    return cos, rel, err
+
+
+# --------------------------------------------------------------------------
+# integer score tiles: bit-exact
+# --------------------------------------------------------------------------
+def _dump_check(w, q, k, tiles, kv_map=None):
+    qz = O.quantize_qk(q, k)
+    nqt = -(-w.seq // 128)
+    for lo, hi in tiles:
+        hi = min(hi, nqt - 1)
+        case(f"debug_qk_int32 {w.name} S={w.seq} D={w.head_dim} tiles {lo}..{hi}")
+        s = A.debug_qk_int32(dev(qz["q_i8"]), dev(qz["k_i8"]), causal=w.causal,
+                             kv_head_map=kv_map, tile_lo=lo, tile_hi=hi, fill=-(1 << 31))
+        torch.cuda.synchronize()
+        got = host(s)
+        rows = np.arange(lo * 128, min((hi + 1) * 128, w.seq))
+        ref = O.scores_i32(qz["q_i8"], qz["k_i8"], causal=w.causal, kv_map=kv_map, rows=rows,
+                           fill=-(1 << 31))
+        g = got[:, :, :len(rows)]
+        assert np.array_equal(g, ref), f"{np.count_nonzero(g != ref)} mismatching scores"
+        # rows beyond S stay untouched
+        assert (got[:, :, len(rows):] == -(1 << 31)).all()
+
+
+@pytest.mark.parametrize("S", [1, 5, 16, 17, 64, 65, 127, 128, 129, 300])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_int32_scores_bitexact_small(S, D, causal):
+    w = small_workload(1, 4, 2, S, D, causal, seed=S + D)
+    q, k, _ = make_qkv(w)
+    nqt = -(-S // 128)
+    _dump_check(w, q, k, [(0, nqt - 1)])
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_int32_scores_bitexact_workloads(name):
+    w = WORKLOADS[name]
+    q, k, _ = make_qkv(w)
+    nqt = -(-w.seq // 128)
+    # the first, a middle and the last query tile of every (batch, head)
+    _dump_check(w, q, k, [(0, 0), (nqt // 2, nqt // 2), (nqt - 1, nqt - 1)])
+
+
+def test_int32_scores_explicit_map():
+    w = small_workload(1, 6, 3, 200, 128, True, seed=77)
+    q, k, _ = make_qkv(w)
+    _dump_check(w, q, k, [(0, 1)], kv_map=[2, 0, 1, 1, 0, 2])
+
+
+# --------------------------------------------------------------------------
+# FP16 path
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("S", TAILS)
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp16_tails_d128_gqa(S, causal):
+    w = small_workload(1, 4, 2, S, 128, causal, seed=1000 + S)
+    q, k, v = make_qkv(w)
+    _fp16_check(w, q, k, v)
+
+
+@pytest.mark.parametrize("S", [1, 2, 15, 16, 17, 64, 65, 128, 129, 1000])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp16_tails_d64_mha(S, causal):
+    w = small_workload(2, 3, 3, S, 64, causal, seed=2000 + S)
+    q, k, v = make_qkv(w)
+    _fp16_check(w, q, k, v)
+
+
+def test_fp16_mqa_and_explicit_map():
+    w = small_workload(1, 8, 1, 333, 128, True, seed=31)
+    q, k, v = make_qkv(w)
+    _fp16_check(w, q, k, v)
+    w2 = small_workload(1, 6, 3, 257, 64, False, seed=32)
+    q, k, v = make_qkv(w2)
+    _fp16_check(w2, q, k, v, kv_map=[2, 0, 1, 1, 0, 2])
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_fp16_workloads_sampled(name):
+    w = WORKLOADS[name]
+    q, k, v = make_qkv(w)
+    rows = None if w.seq <= 256 else sample_rows(w.seq, 24, seed=w.seed)
+    _fp16_check(w, q, k, v, rows=rows)
+
+
+# --------------------------------------------------------------------------
+# INT8 path
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("S", TAILS)
+@pytest.mark.parametrize("causal", [False, True])
+def test_int8_tails_d128_gqa(S, causal):
+    w = small_workload(1, 4, 2, S, 128, causal, seed=3000 + S)
+    q, k, v = make_qkv(w)
+    _int8_check(w, q, k, v)
+
+
+@pytest.mark.parametrize("S", [1, 2, 15, 16, 17, 64, 65, 128, 129, 1000])
+@pytest.mark.parametrize("causal", [False, True])
+def test_int8_tails_d64_mha(S, causal):
+    w = small_workload(2, 3, 3, S, 64, causal, seed=4000 + S)
+    q, k, v = make_qkv(w)
+    _int8_check(w, q, k, v)
+
+
+def test_int8_mqa_and_explicit_map():
+    w = small_workload(1, 8, 1, 333, 128, True, seed=41)
+    q, k, v = make_qkv(w)
+    _int8_check(w, q, k, v)
+    w2 = small_workload(1, 6, 3, 257, 64, False, seed=42)
+    q, k, v = make_qkv(w2)
+    _int8_check(w2, q, k, v, kv_map=[2, 0, 1, 1, 0, 2])
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_int8_workloads_sampled(name):
+    w = WORKLOADS[name]
+    q, k, v = make_qkv(w)
+    rows = None if w.seq <= 256 else sample_rows(w.seq, 24, seed=w.seed)
+    _int8_check(w, q, k, v, rows=rows)
+
+
+# --------------------------------------------------------------------------
+# lse, invariants, determinism, wrappers
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("causal", [False, True])
+def test_lse_both_paths(causal):
+    w = small_workload(1, 4, 2, 300, 128, causal, seed=51)
+    q, k, v = make_qkv(w)
+    case(f"lse causal={causal}")
+    _, lse16 = A.fwd_fp16(dev(q), dev(k), dev(v), causal=causal, return_lse=True)
+    qz = A.quantize_qk(dev(q), dev(k))
+    _, lse8 = A.fwd_int8(qz, dev(v), causal=causal, return_lse=True)
+    torch.cuda.synchronize()
+    _, ref = O.attention(q, k, v, causal=causal, with_lse=True)
+    assert np.abs(host(lse16) - ref).max() < 1e-3
+    qz_h = {key: host(qz[key]) for key in ("q_i8", "q_scale", "k_i8", "k_scale")}
+    _, ref8 = O.quant_attention(qz_h, v, causal=causal, with_lse=True)
+    assert np.abs(host(lse8) - ref8).max() < 1e-3
+
+
+@pytest.mark.parametrize("path", ["fp16", "int8"])
+def test_constant_v_and_causal_row0(path):
+    w = small_workload(1, 4, 2, 777, 128, True, seed=61)
+    q, k, v = make_qkv(w)
+    c = np.float16(0.3330078125)
+    vc = np.full_like(v, c)
+    case(f"invariants {path}")
+    if path == "fp16":
+        out_c = A.fwd_fp16(dev(q), dev(k), dev(vc), causal=True)
+        out = A.fwd_fp16(dev(q), dev(k), dev(v), causal=True)
+    else:
+        qz = A.quantize_qk(dev(q), dev(k))
+        out_c = A.fwd_int8(qz, dev(vc), causal=True)
+        out = A.fwd_int8(qz, dev(v), causal=True)
+    torch.cuda.synchronize()
+    assert np.abs(host(out_c).astype(np.float64) - float(c)).max() <= 2.0 ** -11
+    o = host(out)
+    kv_map = np.arange(4) // 2
+    for h in range(4):
+        assert np.array_equal(o[0, h, 0], v[0, kv_map[h], 0])
+
+
+@pytest.mark.parametrize("path", ["fp16", "int8"])
+def test_runs_are_bitwise_deterministic(path):
+    w = WORKLOADS["batched_mqa"].scaled(batch=4)
+    q, k, v = make_qkv(w)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    case(f"determinism {path}")
+    outs = []
+    for _ in range(3):
+        if path == "fp16":
+            outs.append(A.fwd_fp16(qd, kd, vd, causal=True).clone())
+        else:
+            outs.append(A.fwd_int8(A.quantize_qk(qd, kd), vd, causal=True).clone())
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+def test_gqa_equals_mha_on_repeated_kv_gpu():
+    w = small_workload(1, 8, 2, 300, 128, True, seed=71)
+    q, k, v = make_qkv(w)
+    rk, rv = np.repeat(k, 4, axis=1), np.repeat(v, 4, axis=1)
+    case("gqa == mha(repeated) fp16")
+    a = A.fwd_fp16(dev(q), dev(k), dev(v), causal=True)
+    b = A.fwd_fp16(dev(q), dev(rk), dev(rv), causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_custom_scale_and_sageattn_wrapper():
+    w = small_workload(1, 4, 2, 200, 64, False, seed=81)
+    q, k, v = make_qkv(w)
+    case("custom scale fp16 / sageattn")
+    out = A.fwd_fp16(dev(q), dev(k), dev(v), sm_scale=0.05)
+    ref = O.attention(q, k, v, sm_scale=0.05)
+    torch.cuda.synchronize()
+    assert np.abs(host(out) - ref).max() <= FP16_MAX_ABS
+    s = A.sageattn(dev(q), dev(k), dev(v), is_causal=True, scale=0.1)
+    qz = A.quantize_qk(dev(q), dev(k))
+    t = A.fwd_int8(qz, dev(v), causal=True, sm_scale=0.1)
+    torch.cuda.synchronize()
+    assert torch.equal(s, t)
+    cos, rel = cos_rel_l1(host(s), O.attention(q, k, v, causal=True, sm_scale=0.1))
+    assert cos >= INT8_COS_MIN and rel <= INT8_REL_L1_MAX
