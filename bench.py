@@ -1,0 +1,278 @@
+"""Benchmark of the attention forward hot path on one MI355X.
+
+One step = one pass of the whole hot path over the LLM-prefill workload
+(batch 1, 32 query heads / 8 kv heads, seq 8192, head_dim 128, causal GQA,
+synthetic fp16 inputs already resident in HBM):
+    attn_quantize_qk  (K channel mean, smoothing, per-block INT8 Q/K)
+    attn_fwd_int8     (INT8 QK^T, online softmax, FP16 P.V)
+    attn_fwd_fp16     (the exact FP16 FlashAttention-style baseline)
+
+Printed: ONE JSON line.  `value` is the INT8 (SageAttention-form) path's
+attention throughput, quantisation included: FLOP / (t_quantize + t_fwd_int8),
+with FLOP = 4*B*Hq*S^2*D/2 (causal) and the per-call times taken with HIP
+events on the launch stream inside the timed steps.  The FP16 path and the
+INT8 forward alone are reported beside it, each as TFLOPS and as a fraction
+of MI355X's published dense MFMA peak (fp16 2.5 PFLOP/s, int8 5.0 POP/s).
+
+`roofline` describes the dominant kernel of the step; `cpu_baseline` times the
+CPU oracle (fp64, plain loops) on a bounded sample of the same workload's
+query rows, on this machine's host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+       [--all-workloads] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"fp16": 2500.0, "int8": 5000.0}
+PEAK_BLEND = 2.0 / (1.0 / PEAK_TFLOPS["int8"] + 1.0 / PEAK_TFLOPS["fp16"])
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "llm_prefill_gqa"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--all-workloads", action="store_true",
+                    help="one JSON line per workload (no CPU baseline)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def counters_for(kernel_tag: str, workload: str):
+    """HBM traffic of a kernel from the committed rocprofv3 counter summary, or
+    None when the summary is missing or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_tag}_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    src = os.path.join(ROOT, "bit_quantized_exact_amd", "csrc", vals.get("source", "attn_fwd.hip"))
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if vals.get("source_sha256") != sha:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def run_workload(name, steps, warmup, cpu=False, cpu_seconds=15.0):
+    import torch
+
+    import bit_quantized_exact_amd as A
+    from bit_quantized_exact_amd.inputs import WORKLOADS, make_qkv
+
+    w = WORKLOADS[name]
+    q, k, v = make_qkv(w)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+    # outputs and workspace allocated once: the timed steps only launch kernels
+    qz = A.quantize_qk(qd, kd, with_mean=False)
+    o8 = torch.empty_like(qd)
+    o16 = torch.empty_like(qd)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+
+    def step(evs=None):
+        if evs:
+            evs[0].record(stream)
+        A.quantize_qk(qd, kd, out=qz, with_mean=False)
+        if evs:
+            evs[1].record(stream)
+        A.fwd_int8(qz, vd, causal=w.causal, out=o8)
+        if evs:
+            evs[2].record(stream)
+        A.fwd_fp16(qd, kd, vd, causal=w.causal, out=o16)
+        if evs:
+            evs[3].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    t_q = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    t_8 = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    t_16 = np.array([e[2].elapsed_time(e[3]) for e in ev])
+    ms_q, ms_8, ms_16 = float(t_q.mean()), float(t_8.mean()), float(t_16.mean())
+    flop = w.flops()
+    tf = lambda ms: flop / (ms * 1e-3) / 1e12
+    int8_e2e = tf(ms_q + ms_8)
+
+    # algorithmic bytes (each tensor read or written once)
+    B, Hq, Hkv, S, D = w.batch, w.heads_q, w.heads_kv, w.seq, w.head_dim
+    nq, nk = B * Hq * S * D, B * Hkv * S * D
+    bytes_fp16 = 2 * (2 * nq + 2 * nk)                      # Q, K, V read; O written
+    bytes_int8 = nq + nk + 2 * nk + 2 * nq + 4 * (B * Hq * math.ceil(S / 128) + B * Hkv * math.ceil(S / 64))
+    bytes_quant = 2 * nq + 2 * 2 * nk + nq + nk             # Q once, K twice (sum + quantise), int8 out
+
+    kernels = {
+        "fwd_fp16": dict(ms=ms_16, flop=flop, peak=PEAK_TFLOPS["fp16"], bytes=bytes_fp16),
+        "fwd_int8": dict(ms=ms_8, flop=flop, peak=PEAK_BLEND, bytes=bytes_int8),
+        "quantize_qk": dict(ms=ms_q, flop=0.0, peak=None, bytes=bytes_quant),
+    }
+    dom = max(kernels, key=lambda n: kernels[n]["ms"])
+    kd_ = kernels[dom]
+    if dom == "quantize_qk":
+        achieved = kd_["bytes"] / (kd_["ms"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS}
+    elif dom == "fwd_fp16":
+        achieved = tf(kd_["ms"])
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_TFLOPS["fp16"],
+                "unit": "TFLOP/s", "frac": achieved / PEAK_TFLOPS["fp16"]}
+    else:
+        achieved = tf(kd_["ms"])
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BLEND,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BLEND,
+                "peak_note": "int8 QK^T at 5.0 POP/s and fp16 PV at 2.5 PFLOP/s, harmonic blend"}
+    roof["kernel"] = {"fwd_fp16": "attn_fwd_fp16", "fwd_int8": "attn_fwd_int8",
+                      "quantize_qk": "attn_quantize_qk"}[dom]
+    roof["traffic"] = counters_for(dom, name)
+
+    rec = {
+        "metric": "attention fwd TFLOPS (INT8 & FP16 paths) and % of gfx950 MFMA peak, 1 GPU",
+        "value": round(int8_e2e, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(wall / steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": name, "batch": B, "heads_q": Hq, "heads_kv": Hkv, "seq": S,
+                   "head_dim": D, "causal": w.causal,
+                   "value_is": "INT8 path: FLOP / (t_quantize_qk + t_fwd_int8)"},
+        "paths": {
+            "int8": {"tflops": round(int8_e2e, 2), "ms": round(ms_q + ms_8, 4),
+                     "fwd_only_tflops": round(tf(ms_8), 2), "fwd_ms": round(ms_8, 4),
+                     "quantize_ms": round(ms_q, 4),
+                     "quantize_gbs": round(bytes_quant / (ms_q * 1e-3) / 1e9, 1),
+                     "frac_int8_peak": round(tf(ms_q + ms_8) / PEAK_TFLOPS["int8"], 4),
+                     "frac_blended_peak": round(tf(ms_q + ms_8) / PEAK_BLEND, 4),
+                     "fwd_only_frac_blended_peak": round(tf(ms_8) / PEAK_BLEND, 4)},
+            "fp16": {"tflops": round(tf(ms_16), 2), "ms": round(ms_16, 4),
+                     "frac_fp16_peak": round(tf(ms_16) / PEAK_TFLOPS["fp16"], 4)},
+            "int8_speedup_over_fp16": round(ms_16 / (ms_q + ms_8), 3),
+        },
+        "roofline": {k_: (round(v_, 4) if isinstance(v_, float) else v_) for k_, v_ in roof.items()},
+        "cpu_baseline": None,
+    }
+    if cpu:
+        rec["cpu_baseline"], rec["parity_sample"] = cpu_baseline(w, q, k, v, o8, o16, cpu_seconds)
+    return rec
+
+
+def cpu_baseline(w, q, k, v, o8, o16, target_s):
+    """Time the CPU oracle (fp64 exact attention) on sampled query rows of the
+    same workload and compare the GPU outputs on those rows."""
+    from oracle import oracle as O
+
+    threads = len(os.sched_getaffinity(0))
+    rng = np.random.default_rng([w.seed, 1234])
+
+    def row_flop(rows):
+        vis = (rows + 1) if w.causal else np.full(rows.shape, w.seq)
+        return float(4.0 * w.head_dim * vis.sum() * w.batch * w.heads_q)
+
+    def timed(rows):
+        t = time.perf_counter()
+        out = O.attention(q, k, v, causal=w.causal, rows=rows, nthreads=threads)
+        return out, time.perf_counter() - t
+
+    # calibrate on 16 rows, then size the sample for about target_s seconds
+    cal = np.sort(rng.choice(w.seq, min(w.seq, 16), replace=False)).astype(np.int32)
+    _, tc = timed(cal)
+    n = int(min(w.seq, max(16, 16 * target_s / max(tc, 1e-3))))
+    rows = np.sort(rng.choice(w.seq, n, replace=False)).astype(np.int32)
+    out, dt = timed(rows)
+    fl = row_flop(rows)
+    g8 = o8.cpu().numpy()[:, :, rows].astype(np.float64)
+    g16 = o16.cpu().numpy()[:, :, rows].astype(np.float64)
+    a, b = g8.ravel(), out.ravel()
+    parity = {
+        "rows": int(n) * w.batch * w.heads_q,
+        "fp16_max_abs": float(np.abs(g16 - out).max()),
+        "int8_cos": float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b))),
+        "int8_rel_l1": float(np.abs(a - b).sum() / np.abs(b).sum()),
+    }
+    base = {
+        "value": round(fl / dt / 1e12, 6),
+        "unit": "TFLOPS",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{n} of {w.seq} query rows (uniform random, seeded) of every one of the "
+                   f"{w.batch * w.heads_q} (batch, head) pairs; fp64 exact attention; "
+                   f"{fl / 1e9:.1f} GFLOP in {dt:.2f} s"),
+        "seconds": round(dt, 3),
+    }
+    return base, parity
+
+
+def copy_calibration(nbytes: int):
+    """A plain elementwise copy (torch.neg on fp16) of nbytes, read once and
+    written once: the reference that scales rocprofv3's FETCH_SIZE/WRITE_SIZE."""
+    import torch
+    n = nbytes // 2
+    src = torch.ones(n, dtype=torch.float16, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n * 2, "launches": 3}), flush=True)
+
+
+def main():
+    args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the hot path "
+              "shards by kv-head groups with no communication, so it is measured per GPU.",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.all_workloads:
+        from bit_quantized_exact_amd.inputs import WORKLOADS
+        for name in WORKLOADS:
+            print(json.dumps(run_workload(name, args.steps, args.warmup)), flush=True)
+        return
+    rec = run_workload(args.workload, args.steps, args.warmup, cpu=not args.no_cpu,
+                       cpu_seconds=args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
