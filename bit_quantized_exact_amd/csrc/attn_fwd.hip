@@ -20,30 +20,45 @@
 //     v_mfma_i32_32x32x32_i8 (INT8 path): Q stays in VGPRs as the B operand
 //     for the whole kernel, K tiles are the A operand from LDS.  In the
 //     32x32 accumulator layout a lane then holds ONE query column and 16
-//     keys, so the row max needs a single cross-lane exchange (lane ^ 32) and
+//     keys, so the row max needs one cross-lane swap (v_permlane32_swap) and
 //     the row sum none until the end.
 //   * The output is accumulated transposed too, O^T += V^T P^T: P^T is the
 //     B operand taken straight from the score registers (no data movement),
 //     V^T is the A operand read from a row-major V tile in LDS with
 //     ds_read_b64_tr_b16 (a transposing LDS read), and the accumulator rows
-//     that a lane rescales by alpha all belong to its own query.
-//   * K and V tiles of 64 keys are double-buffered in LDS through registers;
-//     one barrier per key tile.  Row padding keeps the MFMA operand reads and
-//     the transposing reads free of bank conflicts.
+//     that a lane rescales all belong to its own query.
+//   * Software pipeline: while a wave runs the softmax of key tile j on the
+//     VALU, it already issues the MFMAs of the scores of tile j+1, so the
+//     matrix and vector pipes overlap inside one wave (and across the two
+//     waves that share a SIMD).  K tiles are therefore staged one tile ahead
+//     of V tiles; both are double-buffered in LDS through registers, with one
+//     barrier per key tile.  Row padding keeps the MFMA operand reads and the
+//     transposing reads free of bank conflicts.
+//   * Lazy rescaling: the running maximum is only raised (and O, l rescaled)
+//     when a tile's maximum exceeds it by more than 2^8; otherwise the stale
+//     maximum is kept, weights stay <= 2^8 (exact in fp16 range), and the
+//     final O / l is unchanged mathematically.  This removes the per-tile
+//     multiply of the 64 O accumulators per lane in the steady state.
+//   * Branch-free tails: K/V rows beyond the sequence are loaded from the
+//     last row (clamped index) and masked to -inf, so no load is predicated.
 //   * Workgroups are launched XCD-aware: consecutive hardware block ids go
 //     round-robin over the 8 XCDs, so blocks are renumbered such that each
 //     XCD receives a contiguous range of (batch, head) pairs ordered by kv
 //     head; the q-heads of one GQA group then share K/V in that XCD's L2.
 //     Causal launches start with the heaviest (last) query tiles.
 #include "attn_internal.h"
+#include "fwd_geometry.h"
 
 #include <cfloat>
+#include <type_traits>
 
 namespace attn {
 namespace {
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float f2 __attribute__((ext_vector_type(2)));
 typedef float f16x __attribute__((ext_vector_type(16)));
 typedef int i16x __attribute__((ext_vector_type(16)));
 typedef int i4x __attribute__((ext_vector_type(4)));
@@ -51,31 +66,22 @@ typedef __fp16 tr4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
 typedef __attribute__((address_space(3))) tr4 lds_tr4;
 
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazy = 8.0f;   // log2 headroom before the running max is raised
 
 template <int D, bool INT8>
-struct Cfg {
-    static constexpr int KELT = INT8 ? 1 : 2;                 // bytes per K element
-    static constexpr int KROWG = D * KELT;                     // K row bytes in HBM
+struct Cfg : geom::Stage<D, INT8> {
+    using G = geom::Stage<D, INT8>;
+    using G::KELT, G::KROWG, G::KCPR, G::VCPR, G::KPT, G::VPT, G::QSTEPS;
     static constexpr int KROW = KROWG + 16;                    // K row bytes in LDS
     static constexpr int VROW = 2 * D + 64;                    // V row bytes in LDS
     static constexpr int KBYTES = kBN * KROW;
     static constexpr int VBYTES = kBN * VROW;
-    static constexpr int STAGE = KBYTES + VBYTES;
-    static constexpr int KCPR = KROWG / 16;                    // 16-byte chunks per K row
-    static constexpr int VCPR = 2 * D / 16;
-    static constexpr int KPT = kBN * KCPR / kFwdThreads;       // K chunks per thread
-    static constexpr int VPT = kBN * VCPR / kFwdThreads;
-    static constexpr int QSTEPS = INT8 ? D / 32 : D / 16;      // MFMA k-steps over head_dim
     static constexpr int DT = D / 32;                          // 32-row d tiles of O^T
     static_assert(kBN * KCPR % kFwdThreads == 0 && kBN * VCPR % kFwdThreads == 0, "tile split");
+    static_assert(geom::kTileM == kBM && geom::kTileN == kBN && geom::kThreads == kFwdThreads, "geometry");
+    typedef std::conditional_t<INT8, i4x, h8> qfrag_t;         // B operand fragment of Q
+    typedef std::conditional_t<INT8, i16x, f16x> acc_t;        // 32x32 score accumulator
 };
-
-template <bool INT8>
-struct QFrag;
-template <>
-struct QFrag<false> { typedef h8 type; };
-template <>
-struct QFrag<true> { typedef i4x type; };
 
 __device__ __forceinline__ h8 join(tr4 a, tr4 b) {
     h8 r;
@@ -84,12 +90,64 @@ __device__ __forceinline__ h8 join(tr4 a, tr4 b) {
     return r;
 }
 
+__device__ __forceinline__ h8 pack8(float a0, float a1, float a2, float a3, float a4, float a5,
+                                    float a6, float a7) {
+    const h2 p0 = __builtin_convertvector((f2){a0, a1}, h2);
+    const h2 p1 = __builtin_convertvector((f2){a2, a3}, h2);
+    const h2 p2 = __builtin_convertvector((f2){a4, a5}, h2);
+    const h2 p3 = __builtin_convertvector((f2){a6, a7}, h2);
+    const h4 lo = __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
+    const h4 hi = __builtin_shufflevector(p2, p3, 0, 1, 2, 3);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// x combined with the same register of lane ^ 32 (the other half of this
+// lane's query row), without an LDS round trip.
+__device__ __forceinline__ float row_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+    return a > b ? a : b;
+}
+__device__ __forceinline__ float row_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Transposed scores of one 64-key tile for this wave's 32 queries:
+// acc[mt] holds keys mt*32 + (r/4)*8 + (lane/32)*4 + r%4 (register r) of query
+// lane%32.  The same code feeds the forward and the INT32 score dump.
+template <int D, bool INT8>
+__device__ __forceinline__ void score_tile(const char* ks, const typename Cfg<D, INT8>::qfrag_t* qf,
+                                           int l32, int g, typename Cfg<D, INT8>::acc_t acc[2]) {
+    using C = Cfg<D, INT8>;
+    acc[0] = typename C::acc_t{};
+    acc[1] = typename C::acc_t{};
+#pragma unroll
+    for (int s = 0; s < C::QSTEPS; ++s) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            if constexpr (INT8) {
+                const i4x a = *reinterpret_cast<const i4x*>(ks + (mt * 32 + l32) * C::KROW + s * 32 + g * 16);
+                acc[mt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[s], acc[mt], 0, 0, 0);
+            } else {
+                const h8 a = *reinterpret_cast<const h8*>(ks + (mt * 32 + l32) * C::KROW + (s * 16 + g * 8) * 2);
+                acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[s], acc[mt], 0, 0, 0);
+            }
+        }
+    }
+}
+
+using geom::key_offset;
+
 template <int D, bool INT8, bool CAUSAL, bool DUMP>
 __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(const FwdParams p) {
     using C = Cfg<D, INT8>;
-    typedef typename QFrag<INT8>::type qfrag_t;
-    __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
+    typedef typename C::qfrag_t qfrag_t;
+    typedef typename C::acc_t acc_t;
+    __shared__ __attribute__((aligned(16))) char smem[2 * C::KBYTES + (DUMP ? 0 : 2 * C::VBYTES)];
+    auto kbuf = [&](int i) { return smem + i * C::KBYTES; };
+    auto vbuf = [&](int i) { return smem + 2 * C::KBYTES + i * C::VBYTES; };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -99,18 +157,12 @@ void fwd_kernel(const FwdParams p) {
     const int S = p.S;
 
     // ---- block id -> (batch, q-head, query tile), XCD-aware ----
-    const int nblk = gridDim.x;
-    const int bid = blockIdx.x;
-    const int per = nblk >> 3, rem = nblk & 7, xcd = bid & 7;
-    const int L = xcd * per + min(xcd, rem) + (bid >> 3);
-    const int per_b = p.Hq * p.ntiles;
-    const int b = L / per_b;
-    const int rb = L - b * per_b;
-    const int pos = rb / p.ntiles;
-    const int rank = rb - pos * p.ntiles;
-    const int h = p.horder[pos];
+    const geom::BlockCoord bc = geom::decode_block(blockIdx.x, gridDim.x, p.Hq, p.ntiles, p.tile_lo,
+                                                   CAUSAL && !DUMP);
+    const int b = bc.b;
+    const int h = p.horder[bc.pos];
     const int kvh = p.kvmap[h];
-    const int qt = p.tile_lo + ((CAUSAL && !DUMP) ? (p.ntiles - 1 - rank) : rank);
+    const int qt = bc.qt;
 
     const int q0 = qt * kBM;
     const int qw0 = q0 + wave * 32;      // first query row of this wave
@@ -118,165 +170,183 @@ void fwd_kernel(const FwdParams p) {
     const size_t bhq = static_cast<size_t>(b) * p.Hq + h;
     const size_t bhk = static_cast<size_t>(b) * p.Hkv + kvh;
 
-    const int n_end = CAUSAL ? min(S, q0 + kBM) : S;
-    const int nkt = (n_end + kBN - 1) / kBN;
+    const int nkt = geom::block_key_tiles(S, q0, CAUSAL);      // key tiles of the block
+    const int nkt_w = geom::wave_key_tiles(nkt, qw0, CAUSAL);  // key tiles this wave needs
 
-    // ---- Q fragment (B operand of S^T = K Q^T), kept in VGPRs ----
+    // ---- Q fragment (B operand of S^T = K Q^T), kept in VGPRs.  Rows past
+    // the sequence read the last row; they are never stored.
     qfrag_t qf[C::QSTEPS];
     {
         const char* qrow = static_cast<const char*>(p.q) +
-                           (bhq * S + static_cast<size_t>(qi)) * (D * C::KELT);
+                           (bhq * S + static_cast<size_t>(geom::q_row(qi, S))) * (D * C::KELT);
 #pragma unroll
         for (int s = 0; s < C::QSTEPS; ++s) {
             // 16 bytes per lane: int8 elements s*32 + g*16.., or fp16 elements s*16 + g*8..
-            const int off = INT8 ? (s * 32 + g * 16) : (s * 16 + g * 8) * 2;
-            qf[s] = qi < S ? *reinterpret_cast<const qfrag_t*>(qrow + off) : qfrag_t{};
+            qf[s] = *reinterpret_cast<const qfrag_t*>(qrow + C::q_frag_offset(s, g));
         }
     }
 
+    // ---- K / V staging: each thread moves KPT (VPT) 16-byte chunks per tile.
+    // Rows past the sequence are read from row S-1 (always in bounds) and
+    // masked out of the softmax.
     const char* kg = static_cast<const char*>(p.k) + bhk * S * C::KROWG;
-    const char* vg = static_cast<const char*>(p.v) + bhk * S * (2 * D);
-
+    const char* vg = static_cast<const char*>(p.v) + bhk * S * C::VROWG;
+    // Addresses: a wave-uniform tile base plus a 32-bit per-lane offset
+    // (row clamped to the sequence), so the loads use the scalar-base form.
     i4x kreg[C::KPT], vreg[C::VPT];
-    auto gload = [&](int n0) {
+    auto gload_k = [&](int n0) {
+        const int first = geom::tile_first_row(n0, S);
+        const char* base = kg + static_cast<size_t>(first) * C::KROWG;
 #pragma unroll
         for (int i = 0; i < C::KPT; ++i) {
             const int c = tid + kFwdThreads * i;
-            const int row = c / C::KCPR, col = c % C::KCPR;
-            const int key = n0 + row;
-            kreg[i] = key < S ? *reinterpret_cast<const i4x*>(kg + static_cast<size_t>(key) * C::KROWG + col * 16)
-                              : i4x{0, 0, 0, 0};
-        }
-        if constexpr (!DUMP) {   // the score dump reads no V (p.v is null there)
-#pragma unroll
-            for (int i = 0; i < C::VPT; ++i) {
-                const int c = tid + kFwdThreads * i;
-                const int row = c / C::VCPR, col = c % C::VCPR;
-                const int key = n0 + row;
-                vreg[i] = key < S ? *reinterpret_cast<const i4x*>(vg + static_cast<size_t>(key) * (2 * D) + col * 16)
-                                  : i4x{0, 0, 0, 0};
-            }
+            const uint32_t off = static_cast<uint32_t>(geom::tile_lane_row(c / C::KCPR, first, S)) * C::KROWG +
+                                 (c % C::KCPR) * 16;
+            kreg[i] = *reinterpret_cast<const i4x*>(base + off);
         }
     };
-    auto sstore = [&](int stage) {
-        char* ks = smem + stage * C::STAGE;
-        char* vs = ks + C::KBYTES;
+    auto gload_v = [&](int n0) {
+        const int first = geom::tile_first_row(n0, S);
+        const char* base = vg + static_cast<size_t>(first) * C::VROWG;
+#pragma unroll
+        for (int i = 0; i < C::VPT; ++i) {
+            const int c = tid + kFwdThreads * i;
+            const uint32_t off = static_cast<uint32_t>(geom::tile_lane_row(c / C::VCPR, first, S)) * C::VROWG +
+                                 (c % C::VCPR) * 16;
+            vreg[i] = *reinterpret_cast<const i4x*>(base + off);
+        }
+    };
+    auto sstore_k = [&](int stage) {
+        char* ks = kbuf(stage);
 #pragma unroll
         for (int i = 0; i < C::KPT; ++i) {
             const int c = tid + kFwdThreads * i;
             *reinterpret_cast<i4x*>(ks + (c / C::KCPR) * C::KROW + (c % C::KCPR) * 16) = kreg[i];
         }
-        if constexpr (!DUMP) {
+    };
+    auto sstore_v = [&](int stage) {
+        char* vs = vbuf(stage);
 #pragma unroll
-            for (int i = 0; i < C::VPT; ++i) {
-                const int c = tid + kFwdThreads * i;
-                *reinterpret_cast<i4x*>(vs + (c / C::VCPR) * C::VROW + (c % C::VCPR) * 16) = vreg[i];
-            }
+        for (int i = 0; i < C::VPT; ++i) {
+            const int c = tid + kFwdThreads * i;
+            *reinterpret_cast<i4x*>(vs + (c / C::VCPR) * C::VROW + (c % C::VCPR) * 16) = vreg[i];
         }
     };
 
-    float m_run = -INFINITY;   // running row max (log2 units), same in lanes l and l^32
-    float l_run = 0.0f;        // this lane's partial row sum
-    f16x oacc[C::DT];
-#pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) oacc[dt] = f16x{};
+    // Visible keys of a tile at n0 satisfy key_offset(mt, r) < lim for this lane.
+    auto mask_limit = [&](int n0) { return geom::mask_limit(n0, S, qi, g, CAUSAL); };
+    auto tile_needs_mask = [&](int n0) { return (n0 + kBN > S) || (CAUSAL && n0 + kBN - 1 > qw0); };
 
-    float qscale = 0.0f;   // the score dump has no scales (p.q_scale is null there)
-    if constexpr (INT8 && !DUMP) qscale = p.q_scale[bhq * p.nqblk + qt];
-
-    gload(0);
-    sstore(0);
-    __syncthreads();
-
-    for (int it = 0; it < nkt; ++it) {
-        const int n0 = it * kBN;
-        if (it + 1 < nkt) gload(n0 + kBN);
-        const char* ks = smem + (it & 1) * C::STAGE;
-        const char* vs = ks + C::KBYTES;
-        const bool active = !CAUSAL || n0 <= qw0 + 31;
-        if (active) {
-            // ---- S^T tile: 64 keys x 32 queries, two 32x32 MFMA tiles ----
-            float sv[2][16];
-            if constexpr (INT8) {
-                i16x acc[2] = {i16x{}, i16x{}};
-#pragma unroll
-                for (int s = 0; s < C::QSTEPS; ++s) {
-#pragma unroll
-                    for (int mt = 0; mt < 2; ++mt) {
-                        const i4x a = *reinterpret_cast<const i4x*>(ks + (mt * 32 + l32) * C::KROW + s * 32 + g * 16);
-                        acc[mt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[s], acc[mt], 0, 0, 0);
-                    }
-                }
-                if constexpr (DUMP) {
-                    if (qi < S) {
-                        int32_t* orow = p.s_out + (bhq * p.ntiles * kBM + (qi - p.tile_lo * kBM)) * static_cast<size_t>(S);
-#pragma unroll
-                        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                            for (int r = 0; r < 16; ++r) {
-                                const int key = n0 + mt * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-                                if (key < S && (!CAUSAL || key <= qi)) orow[key] = acc[mt][r];
-                            }
-                    }
-                }
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) sv[mt][r] = static_cast<float>(acc[mt][r]);
-            } else {
-                f16x acc[2] = {f16x{}, f16x{}};
-#pragma unroll
-                for (int s = 0; s < C::QSTEPS; ++s) {
-#pragma unroll
-                    for (int mt = 0; mt < 2; ++mt) {
-                        const h8 a = *reinterpret_cast<const h8*>(ks + (mt * 32 + l32) * C::KROW + (s * 16 + g * 8) * 2);
-                        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[s], acc[mt], 0, 0, 0);
-                    }
-                }
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) sv[mt][r] = acc[mt][r];
-            }
-
-            if constexpr (!DUMP) {
-                // scores in log2 units: s * c, c = (dQ dK) sm_scale log2(e)
-                float c = p.scale_log2;
-                if (INT8) c = fmaxf(qscale * p.k_scale[bhk * p.nkblk + it] * p.scale_log2, FLT_MIN);
-                const bool need_mask = (n0 + kBN > S) || (CAUSAL && n0 + kBN - 1 > qw0);
-                if (need_mask) {
+    if constexpr (DUMP) {
+        // ---- INT32 score dump: the same tile code, results written out ----
+        for (int j = 0; j < nkt; ++j) {
+            const int n0 = j * kBN;
+            gload_k(n0);
+            sstore_k(0);
+            __syncthreads();
+            if (j < nkt_w) {   // wave-uniform: the MFMAs run with every lane active
+                acc_t acc[2];
+                score_tile<D, INT8>(kbuf(0), qf, l32, g, acc);
+                if (qi < S) {
+                    int32_t* orow = p.s_out + (bhq * p.ntiles * kBM + (qi - p.tile_lo * kBM)) * static_cast<size_t>(S);
+                    const int lim = mask_limit(n0);
 #pragma unroll
                     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int key = n0 + mt * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-                            if (key >= S || (CAUSAL && key > qi)) sv[mt][r] = -INFINITY;
-                        }
+                        for (int r = 0; r < 16; ++r)
+                            if (key_offset(mt, r) < lim) orow[n0 + g * 4 + key_offset(mt, r)] = acc[mt][r];
+                }
+            }
+            __syncthreads();
+        }
+        return;
+    } else {
+        float m_run = -INFINITY;   // running row max (log2 units); equal in lanes l and l^32
+        float l_run = 0.0f;        // this lane's partial row sum
+        f16x oacc[C::DT];
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) oacc[dt] = f16x{};
+        float qscale = 1.0f;
+        if constexpr (INT8) qscale = p.q_scale[bhq * p.nqblk + qt];
+
+        // ---- prologue: K_0 -> LDS, S_0, then K_1 and V_0 -> LDS ----
+        acc_t sc[2];
+        gload_k(0);
+        sstore_k(0);
+        __syncthreads();
+        score_tile<D, INT8>(kbuf(0), qf, l32, g, sc);
+        gload_k(kBN);
+        gload_v(0);
+        sstore_k(1);
+        sstore_v(0);
+        __syncthreads();
+
+        // ---- main loop: at entry sc holds S_j; LDS holds K_{j+1} and V_j.
+        // Loads and stores run unconditionally (tiles past the end read the
+        // clamped last row into buffers nobody reads): conditional memory ops
+        // make the compiler wait for every outstanding load at the loop head.
+        for (int j = 0; j < nkt; ++j) {
+            const int n0 = j * kBN;
+            gload_k(geom::k_stage_row(j));
+            gload_v(geom::v_stage_row(j));
+            if (j < nkt_w) {
+                // scores in log2 units: s * c with c = (dQ dK) sm_scale log2(e)
+                float c = p.scale_log2;
+                if constexpr (INT8) c = fmaxf(qscale * p.k_scale[bhk * p.nkblk + j] * p.scale_log2, FLT_MIN);
+                float sv[2][16];
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) sv[mt][r] = static_cast<float>(sc[mt][r]);
+                if (tile_needs_mask(n0)) {
+                    const int lim = mask_limit(n0);
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            if (!(key_offset(mt, r) < lim)) sv[mt][r] = -INFINITY;
                 }
                 float mx = sv[0][0];
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv[mt][r]);
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                const float m_new = fmaxf(m_run, mx * c);
-                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-                m_run = m_new;
-                float psum = 0.0f;
-                h8 pb[4];
+                    for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, sv[mt][r]);
+                const float m_tile = row_max(mx) * c;
+                if (__ballot(m_tile > m_run + kLazy)) {
+                    const float m_new = fmaxf(m_run, m_tile);
+                    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                    m_run = m_new;
+                    l_run *= alpha;
+#pragma unroll
+                    for (int dt = 0; dt < C::DT; ++dt) oacc[dt] *= alpha;
+                }
+
+                // scores of the next tile (MFMA) overlap the exponentials (VALU)
+                acc_t sn[2];
+                score_tile<D, INT8>(kbuf((j + 1) & 1), qf, l32, g, sn);
+
+                const float negm = -m_run;
+                float pv[2][16];
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[mt][r], c, -m_new));
-                        psum += pv;
-                        pb[mt * 2 + (r >> 3)][r & 7] = static_cast<_Float16>(pv);
-                    }
-                l_run = l_run * alpha + psum;
+                    for (int r = 0; r < 16; ++r)
+                        pv[mt][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[mt][r], c, negm));
+                float psum = 0.0f;
 #pragma unroll
-                for (int dt = 0; dt < C::DT; ++dt) oacc[dt] *= alpha;
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) psum += pv[mt][r];
+                l_run += psum;
+                h8 pb[4];
+#pragma unroll
+                for (int k4 = 0; k4 < 4; ++k4) {
+                    const float* q = &pv[k4 >> 1][(k4 & 1) * 8];
+                    pb[k4] = pack8(q[0], q[1], q[2], q[3], q[4], q[5], q[6], q[7]);
+                }
 
                 // ---- O^T += V^T P^T ----
+                const char* vs = vbuf(j & 1);
                 const int grp = lane >> 4, li = lane & 15;
 #pragma unroll
                 for (int dt = 0; dt < C::DT; ++dt) {
@@ -284,32 +354,38 @@ void fwd_kernel(const FwdParams p) {
 #pragma unroll
                     for (int k4 = 0; k4 < 4; ++k4) {
                         const int krow = k4 * 16 + g * 4 + (li >> 2);
-                        const tr4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
-                            (lds_tr4*)(vb + krow * C::VROW));
-                        const tr4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
-                            (lds_tr4*)(vb + (krow + 8) * C::VROW));
+                        const tr4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_tr4*)(vb + krow * C::VROW));
+                        const tr4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_tr4*)(vb + (krow + 8) * C::VROW));
                         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(join(lo, hi), pb[k4], oacc[dt], 0, 0, 0);
                     }
                 }
+                // keep the transposing reads ahead of their consumers (4 MFMAs,
+                // or 2 where the FP16 D=128 register budget is tight)
+                __builtin_amdgcn_sched_group_barrier(0x100, (!INT8 && D == 128) ? 4 : 8, 0);
+#pragma unroll
+                for (int i = 0; i < 4 * C::DT; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                }
+                sc[0] = sn[0];
+                sc[1] = sn[1];
             }
+            sstore_k(j & 1);
+            sstore_v((j + 1) & 1);
+            __syncthreads();
         }
-        if (it + 1 < nkt) sstore((it + 1) & 1);
-        __syncthreads();
-    }
 
-    if constexpr (!DUMP) {
-        const float l_tot = l_run + __shfl_xor(l_run, 32);
+        const float l_tot = row_sum(l_run);
         const float inv = 1.0f / l_tot;
         if (qi < S) {
             _Float16* orow = static_cast<_Float16*>(p.o) + (bhq * S + static_cast<size_t>(qi)) * D;
 #pragma unroll
             for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    h4 v;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = static_cast<_Float16>(oacc[dt][j * 4 + e] * inv);
-                    *reinterpret_cast<h4*>(orow + dt * 32 + j * 8 + g * 4) = v;
+                for (int j4 = 0; j4 < 4; ++j4) {
+                    const h2 a = __builtin_convertvector((f2){oacc[dt][j4 * 4 + 0] * inv, oacc[dt][j4 * 4 + 1] * inv}, h2);
+                    const h2 bb = __builtin_convertvector((f2){oacc[dt][j4 * 4 + 2] * inv, oacc[dt][j4 * 4 + 3] * inv}, h2);
+                    *reinterpret_cast<h4*>(orow + geom::o_column(dt, j4, g)) = __builtin_shufflevector(a, bb, 0, 1, 2, 3);
                 }
             if (p.lse && g == 0) p.lse[bhq * S + qi] = (m_run + __builtin_log2f(l_tot)) * kLn2;
         }

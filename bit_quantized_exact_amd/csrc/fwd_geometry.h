@@ -1,0 +1,107 @@
+// Launch geometry and global-memory index arithmetic of the forward kernel.
+//
+// Every global address the forward kernel forms is built from these
+// functions, which compile for the host as well, so that a CPU program can
+// enumerate them for any shape and check that they stay inside the buffers
+// (the geometry check under tests/).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+namespace attn {
+namespace geom {
+
+constexpr int kTileM = 128;   // query rows per workgroup (4 waves x 32)
+constexpr int kTileN = 64;    // keys per tile
+constexpr int kThreads = 256;
+
+__host__ __device__ inline int imin(int a, int b) { return a < b ? a : b; }
+
+struct BlockCoord {
+    int b;    // batch
+    int pos;  // position in the kv-grouped head order
+    int qt;   // query tile
+};
+
+// Hardware block id -> (batch, head position, query tile).  Consecutive
+// hardware ids go round-robin over the 8 XCDs; the renumbering gives each XCD
+// a contiguous range of logical ids.  Causal launches take the heaviest query
+// tiles first.  Bijective on [0, nblk).
+__host__ __device__ inline BlockCoord decode_block(int bid, int nblk, int Hq, int ntiles,
+                                                   int tile_lo, bool heavy_first) {
+    const int per = nblk >> 3, rem = nblk & 7, xcd = bid & 7;
+    const int L = xcd * per + imin(xcd, rem) + (bid >> 3);
+    const int per_b = Hq * ntiles;
+    BlockCoord c;
+    c.b = L / per_b;
+    const int rb = L - c.b * per_b;
+    c.pos = rb / ntiles;
+    const int rank = rb - c.pos * ntiles;
+    c.qt = tile_lo + (heavy_first ? (ntiles - 1 - rank) : rank);
+    return c;
+}
+
+// Key tiles a workgroup visits, and those a wave needs (causal: the wave's
+// last query row bounds its keys).
+__host__ __device__ inline int block_key_tiles(int S, int q0, bool causal) {
+    const int n_end = causal ? imin(S, q0 + kTileM) : S;
+    return (n_end + kTileN - 1) / kTileN;
+}
+__host__ __device__ inline int wave_key_tiles(int nkt, int qw0, bool causal) {
+    return causal ? imin(nkt, (qw0 + 31) / kTileN + 1) : nkt;
+}
+
+// Query row read for a lane: rows past the sequence read the last row.
+__host__ __device__ inline int q_row(int qi, int S) { return imin(qi, S - 1); }
+
+// Staging of one key tile at n0 (n0 may lie past the sequence end: the
+// pipeline prefetches two tiles ahead).  The wave-uniform part is the first
+// row of the tile clamped to S-1; each lane adds a row clamped to the rows
+// that remain, so every row read lies in [0, S-1].
+__host__ __device__ inline int tile_first_row(int n0, int S) { return imin(n0, S - 1); }
+__host__ __device__ inline int tile_lane_row(int row, int first_row, int S) {
+    return imin(row, S - 1 - first_row);
+}
+
+// Global-memory layout of one head's tiles: row bytes, 16-byte chunks per
+// row, chunks per thread and per-lane Q fragment bytes.
+template <int D, bool INT8>
+struct Stage {
+    static constexpr int KELT = INT8 ? 1 : 2;          // bytes per Q/K element
+    static constexpr int KROWG = D * KELT;             // Q/K row bytes
+    static constexpr int VROWG = 2 * D;                // V / O row bytes
+    static constexpr int KCPR = KROWG / 16;            // 16-byte chunks per K row
+    static constexpr int VCPR = VROWG / 16;
+    static constexpr int KPT = kTileN * KCPR / kThreads;
+    static constexpr int VPT = kTileN * VCPR / kThreads;
+    static constexpr int QSTEPS = INT8 ? D / 32 : D / 16;
+    // byte offset within a Q row of the 16-byte fragment for MFMA k-step s, lane half g
+    __host__ __device__ static constexpr int q_frag_offset(int s, int g) {
+        return INT8 ? (s * 32 + g * 16) : (s * 16 + g * 8) * 2;
+    }
+};
+
+// Score register r of 32-key sub-tile mt (32x32 MFMA accumulator layout)
+// holds key n0 + g*4 + key_offset(mt, r) of a tile at n0 (g = lane / 32).
+__host__ __device__ constexpr int key_offset(int mt, int r) { return mt * 32 + (r >> 2) * 8 + (r & 3); }
+
+// Keys of the tile at n0 visible to query qi satisfy key_offset < mask_limit:
+// key < S, and key <= qi when causal.
+__host__ __device__ inline int mask_limit(int n0, int S, int qi, int g, bool causal) {
+    int lim = S - n0 - g * 4;
+    if (causal) lim = imin(lim, qi - n0 - g * 4 + 1);
+    return lim;
+}
+
+// Output column of accumulator group j4 (4 consecutive registers) of d-tile dt.
+__host__ __device__ constexpr int o_column(int dt, int j4, int g) { return dt * 32 + j4 * 8 + g * 4; }
+
+// Pipeline schedule: the prologue stages K tiles 0 and 1 and V tile 0;
+// iteration j of the main loop stages K tile j+2 and V tile j+1.
+__host__ __device__ inline int k_stage_row(int j) { return (j + 2) * kTileN; }
+__host__ __device__ inline int v_stage_row(int j) { return (j + 1) * kTileN; }
+
+}  // namespace geom
+}  // namespace attn

@@ -1,0 +1,171 @@
+// CPU check of the forward kernel's global-memory index arithmetic.
+//
+// Built for the host only (the shared helpers are __host__ __device__) and
+// run by tests/test_geometry.py.  For every shape it enumerates, per
+// workgroup, wave and lane, each global address the kernel forms (Q
+// fragments, staged K/V tile rows for the whole pipeline schedule including
+// the tiles prefetched past the end, scale indices, output columns and the
+// score-dump indices) and checks that it lies inside its buffer.  It also
+// checks that the block renumbering is a bijection.  Exit status 0 = clean.
+#include "fwd_geometry.h"
+
+#include <cstdio>
+#include <cstdlib>
+#include <vector>
+
+using namespace attn::geom;
+
+static long g_errors = 0;
+#define REQUIRE(cond, ...)                                                \
+    do {                                                                  \
+        if (!(cond)) {                                                    \
+            if (g_errors < 20) {                                          \
+                std::printf("FAIL %s:%d: %s | ", __FILE__, __LINE__, #cond); \
+                std::printf(__VA_ARGS__);                                 \
+                std::printf("\n");                                        \
+            }                                                             \
+            ++g_errors;                                                   \
+        }                                                                 \
+    } while (0)
+
+template <int D, bool INT8>
+static void check_shape(int B, int Hq, int S, bool causal, bool dump, int tile_lo, int ntiles,
+                        bool all_heads) {
+    using St = Stage<D, INT8>;
+    const int nqt = (S + kTileM - 1) / kTileM;
+    if (!dump) {
+        tile_lo = 0;
+        ntiles = nqt;
+    }
+    const long nblk = static_cast<long>(B) * Hq * ntiles;
+    const size_t qk_head_bytes = static_cast<size_t>(S) * St::KROWG;
+    const size_t v_head_bytes = static_cast<size_t>(S) * St::VROWG;
+    const int nqblk = (S + 127) / 128, nkblk = (S + 63) / 64;
+    std::vector<char> seen(nblk, 0);
+    for (long bid = 0; bid < nblk; ++bid) {
+        const BlockCoord c = decode_block(static_cast<int>(bid), static_cast<int>(nblk), Hq, ntiles,
+                                          tile_lo, causal && !dump);
+        REQUIRE(c.b >= 0 && c.b < B && c.pos >= 0 && c.pos < Hq && c.qt >= tile_lo &&
+                    c.qt < tile_lo + ntiles && c.qt < nqt,
+                "bid %ld -> b %d pos %d qt %d", bid, c.b, c.pos, c.qt);
+        if (!(c.b >= 0 && c.b < B && c.pos >= 0 && c.pos < Hq && c.qt >= tile_lo && c.qt < tile_lo + ntiles))
+            continue;
+        const long slot = (static_cast<long>(c.b) * Hq + c.pos) * ntiles + (c.qt - tile_lo);
+        REQUIRE(!seen[slot], "bid %ld maps to a taken slot", bid);
+        seen[slot] = 1;
+        if (!all_heads && !((c.b == 0 && c.pos == 0) || (c.b == B - 1 && c.pos == Hq - 1))) continue;
+
+        const int q0 = c.qt * kTileM;
+        const int nkt = block_key_tiles(S, q0, causal);
+        REQUIRE(nkt >= 1 && nkt <= nkblk, "nkt %d nkblk %d", nkt, nkblk);
+        REQUIRE(c.qt < nqblk, "q scale index %d of %d", c.qt, nqblk);
+        for (int wave = 0; wave < 4; ++wave) {
+            const int qw0 = q0 + wave * 32;
+            const int nkt_w = wave_key_tiles(nkt, qw0, causal);
+            REQUIRE(nkt_w >= 1 && nkt_w <= nkt, "nkt_w %d nkt %d", nkt_w, nkt);
+            for (int lane = 0; lane < 64; ++lane) {
+                const int qi = qw0 + (lane & 31), g = lane >> 5;
+                const int qr = q_row(qi, S);
+                REQUIRE(qr >= 0 && qr < S, "q row %d S %d", qr, S);
+                for (int s = 0; s < St::QSTEPS; ++s) {
+                    const int off = St::q_frag_offset(s, g);
+                    REQUIRE(off >= 0 && off + 16 <= St::KROWG, "q frag offset %d", off);
+                }
+                if (!dump && qi < S)
+                    for (int dt = 0; dt < D / 32; ++dt)
+                        for (int j4 = 0; j4 < 4; ++j4) {
+                            const int col = o_column(dt, j4, g);
+                            REQUIRE(col >= 0 && col + 4 <= D, "o column %d", col);
+                        }
+                if (dump && qi < S)
+                    for (int j = 0; j < nkt_w; ++j) {
+                        const int n0 = j * kTileN;
+                        const int lim = mask_limit(n0, S, qi, g, causal);
+                        for (int mt = 0; mt < 2; ++mt)
+                            for (int r = 0; r < 16; ++r)
+                                if (key_offset(mt, r) < lim) {
+                                    const int key = n0 + g * 4 + key_offset(mt, r);
+                                    REQUIRE(key >= 0 && key < S && (!causal || key <= qi), "dump key %d", key);
+                                    const int row = qi - tile_lo * kTileM;
+                                    REQUIRE(row >= 0 && row < ntiles * kTileM, "dump row %d", row);
+                                }
+                    }
+                for (int j = 0; j < nkt_w; ++j) REQUIRE(j < nkblk, "k scale index %d", j);
+            }
+        }
+        // staged tiles, in the pipeline order of the kernel
+        std::vector<int> kn0, vn0;
+        if (dump) {
+            for (int j = 0; j < nkt; ++j) kn0.push_back(j * kTileN);
+        } else {
+            kn0 = {0, kTileN};
+            vn0 = {0};
+            for (int j = 0; j < nkt; ++j) {
+                kn0.push_back(k_stage_row(j));
+                vn0.push_back(v_stage_row(j));
+            }
+        }
+        for (int n0 : kn0) {
+            const int first = tile_first_row(n0, S);
+            REQUIRE(first >= 0 && first <= S - 1, "k first row %d (n0 %d, S %d)", first, n0, S);
+            for (int tid = 0; tid < kThreads; ++tid)
+                for (int i = 0; i < St::KPT; ++i) {
+                    const int cidx = tid + kThreads * i;
+                    const int row = tile_lane_row(cidx / St::KCPR, first, S);
+                    const long long off32 = static_cast<long long>(row) * St::KROWG + (cidx % St::KCPR) * 16;
+                    REQUIRE(row >= 0 && first + row <= S - 1, "k row %d first %d S %d", row, first, S);
+                    REQUIRE(off32 >= 0 && off32 < (1LL << 32), "k lane offset %lld", off32);
+                    const size_t off = static_cast<size_t>(first) * St::KROWG + static_cast<size_t>(off32);
+                    REQUIRE(off + 16 <= qk_head_bytes, "k byte %zu of %zu", off, qk_head_bytes);
+                }
+        }
+        for (int n0 : vn0) {
+            const int first = tile_first_row(n0, S);
+            REQUIRE(first >= 0 && first <= S - 1, "v first row %d", first);
+            for (int tid = 0; tid < kThreads; ++tid)
+                for (int i = 0; i < St::VPT; ++i) {
+                    const int cidx = tid + kThreads * i;
+                    const int row = tile_lane_row(cidx / St::VCPR, first, S);
+                    const long long off32 = static_cast<long long>(row) * St::VROWG + (cidx % St::VCPR) * 16;
+                    REQUIRE(row >= 0 && first + row <= S - 1, "v row %d first %d S %d", row, first, S);
+                    REQUIRE(off32 >= 0 && off32 < (1LL << 32), "v lane offset %lld", off32);
+                    const size_t off = static_cast<size_t>(first) * St::VROWG + static_cast<size_t>(off32);
+                    REQUIRE(off + 16 <= v_head_bytes, "v byte %zu of %zu", off, v_head_bytes);
+                }
+        }
+    }
+    for (long i = 0; i < nblk; ++i) REQUIRE(seen[i], "slot %ld never visited", i);
+}
+
+template <int D>
+static void check_all_paths(int B, int Hq, int S, bool all_heads) {
+    const int nqt = (S + kTileM - 1) / kTileM;
+    for (int causal = 0; causal < 2; ++causal) {
+        check_shape<D, false>(B, Hq, S, causal, false, 0, 0, all_heads);
+        check_shape<D, true>(B, Hq, S, causal, false, 0, 0, all_heads);
+        check_shape<D, true>(B, Hq, S, causal, true, 0, nqt, all_heads);
+        check_shape<D, true>(B, Hq, S, causal, true, nqt - 1, 1, all_heads);
+        check_shape<D, true>(B, Hq, S, causal, true, nqt / 2, (nqt + 1) / 2 - nqt / 2 + 1 > 0 ? 1 : 1, all_heads);
+    }
+}
+
+int main() {
+    long shapes = 0;
+    for (int S = 1; S <= 300; ++S) {
+        check_all_paths<64>(1, 3, S, true);
+        check_all_paths<128>(2, 2, S, true);
+        shapes += 2;
+    }
+    const int big[] = {511, 512, 513, 1000, 1023, 1024, 1025, 4095, 4096, 4097, 8192, 16384, 32768};
+    for (int S : big) {
+        check_all_paths<64>(2, 3, S, S <= 4097);
+        check_all_paths<128>(1, 5, S, S <= 4097);
+        shapes += 2;
+    }
+    // many blocks (grid sizes that are not multiples of 8, large batch)
+    check_all_paths<128>(64, 16, 1024, false);
+    check_all_paths<64>(3, 7, 777, true);
+    shapes += 2;
+    std::printf("checked %ld shape families, %ld errors\n", shapes, g_errors);
+    return g_errors == 0 ? 0 : 1;
+}
