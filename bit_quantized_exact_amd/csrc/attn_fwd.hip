@@ -193,8 +193,10 @@ void fwd_kernel(const FwdParams p) {
     const char* vg = static_cast<const char*>(p.v) + bhk * S * C::VROWG;
     // Addresses: a wave-uniform tile base plus a 32-bit per-lane offset
     // (row clamped to the sequence), so the loads use the scalar-base form.
-    i4x kreg[C::KPT], vreg[C::VPT];
-    auto gload_k = [&](int n0) {
+    // Register sets for staging (a second set when prefetching two tiles ahead).
+    constexpr int DEPTH = DUMP ? 1 : geom::fwd_prefetch_depth(D, INT8);
+    i4x kreg[DEPTH][C::KPT], vreg[DEPTH][C::VPT];
+    auto gload_k = [&](int n0, i4x (&dst)[C::KPT]) {
         const int first = geom::tile_first_row(n0, S);
         const char* base = kg + static_cast<size_t>(first) * C::KROWG;
 #pragma unroll
@@ -202,10 +204,10 @@ void fwd_kernel(const FwdParams p) {
             const int c = tid + kFwdThreads * i;
             const uint32_t off = static_cast<uint32_t>(geom::tile_lane_row(c / C::KCPR, first, S)) * C::KROWG +
                                  (c % C::KCPR) * 16;
-            kreg[i] = *reinterpret_cast<const i4x*>(base + off);
+            dst[i] = *reinterpret_cast<const i4x*>(base + off);
         }
     };
-    auto gload_v = [&](int n0) {
+    auto gload_v = [&](int n0, i4x (&dst)[C::VPT]) {
         const int first = geom::tile_first_row(n0, S);
         const char* base = vg + static_cast<size_t>(first) * C::VROWG;
 #pragma unroll
@@ -213,23 +215,23 @@ void fwd_kernel(const FwdParams p) {
             const int c = tid + kFwdThreads * i;
             const uint32_t off = static_cast<uint32_t>(geom::tile_lane_row(c / C::VCPR, first, S)) * C::VROWG +
                                  (c % C::VCPR) * 16;
-            vreg[i] = *reinterpret_cast<const i4x*>(base + off);
+            dst[i] = *reinterpret_cast<const i4x*>(base + off);
         }
     };
-    auto sstore_k = [&](int stage) {
+    auto sstore_k = [&](int stage, const i4x (&src)[C::KPT]) {
         char* ks = kbuf(stage);
 #pragma unroll
         for (int i = 0; i < C::KPT; ++i) {
             const int c = tid + kFwdThreads * i;
-            *reinterpret_cast<i4x*>(ks + (c / C::KCPR) * C::KROW + (c % C::KCPR) * 16) = kreg[i];
+            *reinterpret_cast<i4x*>(ks + (c / C::KCPR) * C::KROW + (c % C::KCPR) * 16) = src[i];
         }
     };
-    auto sstore_v = [&](int stage) {
+    auto sstore_v = [&](int stage, const i4x (&src)[C::VPT]) {
         char* vs = vbuf(stage);
 #pragma unroll
         for (int i = 0; i < C::VPT; ++i) {
             const int c = tid + kFwdThreads * i;
-            *reinterpret_cast<i4x*>(vs + (c / C::VCPR) * C::VROW + (c % C::VCPR) * 16) = vreg[i];
+            *reinterpret_cast<i4x*>(vs + (c / C::VCPR) * C::VROW + (c % C::VCPR) * 16) = src[i];
         }
     };
 
@@ -241,8 +243,8 @@ void fwd_kernel(const FwdParams p) {
         // ---- INT32 score dump: the same tile code, results written out ----
         for (int j = 0; j < nkt; ++j) {
             const int n0 = j * kBN;
-            gload_k(n0);
-            sstore_k(0);
+            gload_k(n0, kreg[0]);
+            sstore_k(0, kreg[0]);
             __syncthreads();
             if (j < nkt_w) {   // wave-uniform: the MFMAs run with every lane active
                 acc_t acc[2];
@@ -269,26 +271,35 @@ void fwd_kernel(const FwdParams p) {
         float qscale = 1.0f;
         if constexpr (INT8) qscale = p.q_scale[bhq * p.nqblk + qt];
 
-        // ---- prologue: K_0 -> LDS, S_0, then K_1 and V_0 -> LDS ----
+        // ---- prologue: K_0 -> LDS, S_0, then K_1 and V_0 -> LDS (and, at
+        // depth 2, K_2 and V_1 into the second register set) ----
         acc_t sc[2];
-        gload_k(0);
-        sstore_k(0);
+        gload_k(0, kreg[0]);
+        sstore_k(0, kreg[0]);
         __syncthreads();
         score_tile<D, INT8>(kbuf(0), qf, l32, g, sc);
-        gload_k(kBN);
-        gload_v(0);
-        sstore_k(1);
-        sstore_v(0);
+        gload_k(kBN, kreg[0]);
+        gload_v(0, vreg[0]);
+        sstore_k(1, kreg[0]);
+        sstore_v(0, vreg[0]);
+        if constexpr (DEPTH == 2) {
+            gload_k(2 * kBN, kreg[DEPTH - 1]);
+            gload_v(kBN, vreg[DEPTH - 1]);
+        }
         __syncthreads();
 
         // ---- main loop: at entry sc holds S_j; LDS holds K_{j+1} and V_j.
         // Loads and stores run unconditionally (tiles past the end read the
         // clamped last row into buffers nobody reads): conditional memory ops
         // make the compiler wait for every outstanding load at the loop head.
-        for (int j = 0; j < nkt; ++j) {
+        // Iteration j loads into set LS and writes set SS to LDS (the same set
+        // at depth 1; the set loaded one iteration earlier at depth 2).
+        auto step = [&](int j, auto ls_tag) {
+            constexpr int LS = decltype(ls_tag)::value;
+            constexpr int SS = DEPTH == 2 ? 1 - LS : LS;
             const int n0 = j * kBN;
-            gload_k(geom::k_stage_row(j));
-            gload_v(geom::v_stage_row(j));
+            gload_k(geom::k_load_row<DEPTH>(j), kreg[LS]);
+            gload_v(geom::v_load_row<DEPTH>(j), vreg[LS]);
             if (j < nkt_w) {
                 // scores in log2 units: s * c with c = (dQ dK) sm_scale log2(e)
                 float c = p.scale_log2;
@@ -370,9 +381,18 @@ void fwd_kernel(const FwdParams p) {
                 sc[0] = sn[0];
                 sc[1] = sn[1];
             }
-            sstore_k(j & 1);
-            sstore_v((j + 1) & 1);
+            sstore_k(j & 1, kreg[SS]);
+            sstore_v((j + 1) & 1, vreg[SS]);
             __syncthreads();
+        };
+        if constexpr (DEPTH == 2) {
+            const int iters = geom::loop_iterations<2>(nkt);
+            for (int j = 0; j < iters; j += 2) {
+                step(j, std::integral_constant<int, 0>{});
+                step(j + 1, std::integral_constant<int, 1>{});
+            }
+        } else {
+            for (int j = 0; j < nkt; ++j) step(j, std::integral_constant<int, 0>{});
         }
 
         const float l_tot = row_sum(l_run);

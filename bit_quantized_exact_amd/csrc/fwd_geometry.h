@@ -98,10 +98,21 @@ __host__ __device__ inline int mask_limit(int n0, int S, int qi, int g, bool cau
 // Output column of accumulator group j4 (4 consecutive registers) of d-tile dt.
 __host__ __device__ constexpr int o_column(int dt, int j4, int g) { return dt * 32 + j4 * 8 + g * 4; }
 
-// Pipeline schedule: the prologue stages K tiles 0 and 1 and V tile 0;
-// iteration j of the main loop stages K tile j+2 and V tile j+1.
-__host__ __device__ inline int k_stage_row(int j) { return (j + 2) * kTileN; }
-__host__ __device__ inline int v_stage_row(int j) { return (j + 1) * kTileN; }
+// Pipeline schedule.  K tiles are consumed one iteration before V tiles.
+// With prefetch depth DEPTH (1 or 2), iteration j of the main loop issues
+// the global loads of K tile j+1+DEPTH and V tile j+DEPTH into registers and
+// writes the tiles loaded DEPTH-1 iterations earlier (K tile j+2, V tile
+// j+1) to LDS.  The prologue loads K tiles 0..DEPTH and V tiles 0..DEPTH-1.
+// At depth 2 the loop runs an even number of iterations (two register sets
+// alternate); an iteration past the last tile only stages clamped rows.
+// Depth 2 needs a second register set; FP16 at head_dim 128 has no room for it.
+__host__ __device__ constexpr int fwd_prefetch_depth(int D, bool int8) { return (!int8 && D == 128) ? 1 : 2; }
+template <int DEPTH>
+__host__ __device__ inline int k_load_row(int j) { return (j + 1 + DEPTH) * kTileN; }
+template <int DEPTH>
+__host__ __device__ inline int v_load_row(int j) { return (j + DEPTH) * kTileN; }
+template <int DEPTH>
+__host__ __device__ inline int loop_iterations(int nkt) { return DEPTH == 2 ? (nkt + 1) & ~1 : nkt; }
 
 }  // namespace geom
 }  // namespace attn

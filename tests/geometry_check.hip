@@ -98,11 +98,13 @@ static void check_shape(int B, int Hq, int S, bool causal, bool dump, int tile_l
         if (dump) {
             for (int j = 0; j < nkt; ++j) kn0.push_back(j * kTileN);
         } else {
-            kn0 = {0, kTileN};
-            vn0 = {0};
-            for (int j = 0; j < nkt; ++j) {
-                kn0.push_back(k_stage_row(j));
-                vn0.push_back(v_stage_row(j));
+            const int depth = fwd_prefetch_depth(D, INT8);
+            for (int t = 0; t <= depth; ++t) kn0.push_back(t * kTileN);
+            for (int t = 0; t < depth; ++t) vn0.push_back(t * kTileN);
+            const int iters = depth == 2 ? loop_iterations<2>(nkt) : loop_iterations<1>(nkt);
+            for (int j = 0; j < iters; ++j) {
+                kn0.push_back(depth == 2 ? k_load_row<2>(j) : k_load_row<1>(j));
+                vn0.push_back(depth == 2 ? v_load_row<2>(j) : v_load_row<1>(j));
             }
         }
         for (int n0 : kn0) {
