@@ -6,10 +6,13 @@ stream) and calls the C ABI of the same name; all arithmetic runs in the HIP
 kernels.  torch provides device memory and streams.
 
     attn_quantize_qk -> quantize_qk     K smoothing + per-block INT8 Q/K
+    attn_quantize_k  -> quantize_k      K smoothing + per-block INT8 K only
     attn_fwd_int8    -> fwd_int8        INT8 QK^T, FP16 PV, online softmax
+    attn_fwd_int8_fused_q -> fwd_int8_fused_q   the same, quantising Q in the kernel
     attn_fwd_fp16    -> fwd_fp16        exact FP16 FlashAttention-style forward
     attn_debug_qk_int32 -> debug_qk_int32   the INT32 score tiles (test hook)
-    sageattn(q, k, v, is_causal, scale)     one-call scaled_dot_product_attention replacement
+    sageattn(q, k, v, is_causal, scale)     one-call scaled_dot_product_attention
+                                            replacement (quantize_k + fwd_int8_fused_q)
 
 Sources: SageAttention article ("又快又准，即插即用！清华8比特量化Attention…"),
 技术方案 and its plug-and-play example; "注意力即一切：从 MHA 到 GQA" §2.2-§5.1.
@@ -25,8 +28,9 @@ from . import _native
 from ._native import AttnShape, lib
 
 __all__ = [
-    "AttnError", "quant_blocks", "quantize_workspace_bytes", "quantize_qk", "fwd_int8",
-    "fwd_fp16", "debug_qk_int32", "sageattn", "status_string", "AttnShape", "lib",
+    "AttnError", "quant_blocks", "quantize_workspace_bytes", "quantize_qk", "quantize_k",
+    "fwd_int8", "fwd_int8_fused_q", "fwd_fp16", "debug_qk_int32", "sageattn", "status_string",
+    "AttnShape", "lib",
 ]
 
 
@@ -125,6 +129,68 @@ def quantize_qk(q: torch.Tensor, k: torch.Tensor, *, out: Optional[dict] = None,
     return o
 
 
+def quantize_k(k: torch.Tensor, *, out: Optional[dict] = None,
+               workspace: Optional[torch.Tensor] = None, with_mean: bool = True, stream=None):
+    """K smoothing + per-block INT8 quantisation of K only.  Returns a dict with
+    k_i8, k_scale, k_mean (None unless with_mean) and workspace."""
+    _dev(k, torch.float16, "k")
+    if k.dim() != 4:
+        raise ValueError("k must be [batch, heads, seq, head_dim]")
+    B, Hkv, S, D = k.shape
+    sh = AttnShape(B, Hkv, Hkv, S, D)
+    _, bk = quant_blocks()
+    o = dict(out) if out is not None else {}
+    dev = k.device
+    if "k_i8" not in o:
+        o["k_i8"] = torch.empty((B, Hkv, S, D), dtype=torch.int8, device=dev)
+        o["k_scale"] = torch.empty((B, Hkv, -(-S // bk)), dtype=torch.float32, device=dev)
+    if with_mean and o.get("k_mean") is None:
+        o["k_mean"] = torch.empty((B, Hkv, D), dtype=torch.float32, device=dev)
+    if not with_mean:
+        o["k_mean"] = None
+    nbytes = quantize_workspace_bytes(sh)
+    if nbytes == 0:
+        raise AttnError(_native.ATTN_EINVAL, "attn_quantize_workspace_bytes")
+    if workspace is None:
+        workspace = o.get("workspace")
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    o["workspace"] = workspace
+    _check(lib().attn_quantize_k(ctypes.byref(sh), _ptr(k), _ptr(o["k_i8"]), _ptr(o["k_scale"]),
+                                 _ptr(o["k_mean"]), _ptr(workspace), _stream(stream)),
+           "attn_quantize_k")
+    return o
+
+
+def fwd_int8_fused_q(q: torch.Tensor, kz: dict, v: torch.Tensor, *, causal: bool = False,
+                     kv_head_map=None, sm_scale: Optional[float] = None,
+                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                     return_lse: bool = False, q_scale_out: Optional[torch.Tensor] = None,
+                     stream=None):
+    """8-bit attention forward reading fp16 Q and quantising it in the kernel;
+    kz is the output of quantize_k (or quantize_qk)."""
+    _dev(q, torch.float16, "q")
+    k_i8 = _dev(kz["k_i8"], torch.int8, "k_i8")
+    ks = _dev(kz["k_scale"], torch.float32, "k_scale")
+    _dev(v, torch.float16, "v")
+    sh = _shape(q, k_i8)
+    if tuple(v.shape) != tuple(k_i8.shape):
+        raise ValueError("v must have the shape of k")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, torch.float16, "out")
+    if return_lse and lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    if q_scale_out is not None:
+        _dev(q_scale_out, torch.float32, "q_scale_out")
+    _keep, mp = _map_arg(kv_head_map)
+    _check(lib().attn_fwd_int8_fused_q(ctypes.byref(sh), _ptr(q), _ptr(k_i8), _ptr(ks), _ptr(v),
+                                       _ptr(out), _ptr(lse), _ptr(q_scale_out), mp,
+                                       int(bool(causal)), float(sm_scale or 0.0), _stream(stream)),
+           "attn_fwd_int8_fused_q")
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
 def fwd_int8(qz: dict, v: torch.Tensor, *, causal: bool = False, kv_head_map=None,
              sm_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
              lse: Optional[torch.Tensor] = None, return_lse: bool = False, stream=None):
@@ -194,7 +260,8 @@ def debug_qk_int32(q_i8: torch.Tensor, k_i8: torch.Tensor, *, causal: bool = Fal
 def sageattn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: bool = False,
              scale: Optional[float] = None, kv_head_map=None) -> torch.Tensor:
     """Drop-in for torch's scaled_dot_product_attention on fp16 [B, H, S, D]
-    tensors (the SageAttention article's plug-and-play use): smoothing and
-    INT8 quantisation of Q/K, then the 8-bit fused forward."""
-    qz = quantize_qk(q.contiguous(), k.contiguous(), with_mean=False)
-    return fwd_int8(qz, v.contiguous(), causal=is_causal, kv_head_map=kv_head_map, sm_scale=scale)
+    tensors (the SageAttention article's plug-and-play use): K smoothing and
+    INT8 quantisation of K, then the 8-bit forward that quantises Q itself."""
+    kz = quantize_k(k.contiguous(), with_mean=False)
+    return fwd_int8_fused_q(q.contiguous(), kz, v.contiguous(), causal=is_causal,
+                            kv_head_map=kv_head_map, sm_scale=scale)

@@ -19,8 +19,9 @@ ATTN_MAX_HEADS = 256
 ATTN_MAX_SEQ = 1 << 22
 
 EXPORTED = (
-    "attn_quant_blocks", "attn_quantize_workspace_bytes", "attn_quantize_qk",
-    "attn_fwd_int8", "attn_fwd_fp16", "attn_debug_qk_int32", "attn_status_string",
+    "attn_quant_blocks", "attn_quantize_workspace_bytes", "attn_quantize_qk", "attn_quantize_k",
+    "attn_fwd_int8", "attn_fwd_int8_fused_q", "attn_fwd_fp16", "attn_debug_qk_int32",
+    "attn_status_string",
 )
 
 
@@ -53,6 +54,10 @@ def lib():
     L.attn_quantize_qk.restype = ctypes.c_int
     L.attn_fwd_int8.argtypes = [SP, P, P, P, P, P, P, P, P, ctypes.c_int, F32, P]
     L.attn_fwd_int8.restype = ctypes.c_int
+    L.attn_quantize_k.argtypes = [SP, P, P, P, P, P, P]
+    L.attn_quantize_k.restype = ctypes.c_int
+    L.attn_fwd_int8_fused_q.argtypes = [SP, P, P, P, P, P, P, P, P, ctypes.c_int, F32, P]
+    L.attn_fwd_int8_fused_q.restype = ctypes.c_int
     L.attn_fwd_fp16.argtypes = [SP, P, P, P, P, P, P, ctypes.c_int, F32, P]
     L.attn_fwd_fp16.restype = ctypes.c_int
     L.attn_debug_qk_int32.argtypes = [SP, P, P, P, ctypes.c_int, I32, I32, P, P]

@@ -107,6 +107,48 @@ int attn_quantize_qk(const attn_shape* shape, const void* q_f16, const void* k_f
                            static_cast<hipStream_t>(stream));
 }
 
+int attn_quantize_k(const attn_shape* shape, const void* k_f16, int8_t* k_i8, float* k_scale,
+                    float* k_mean, void* workspace, void* stream) {
+    int st = check_shape(shape);
+    if (st != ATTN_OK) return st;
+    if (!k_f16 || !k_i8 || !k_scale || !workspace) return ATTN_EINVAL;
+    if (!aligned(k_f16, 16) || !aligned(k_i8, 16) || !aligned(workspace, 16) || !aligned(k_scale, 4) ||
+        (k_mean && !aligned(k_mean, 4)))
+        return ATTN_EINVAL;
+    size_t mean_off = 0;
+    QuantWorkspace ws;
+    quant_workspace_layout(*shape, &mean_off, &ws.nchunk);
+    ws.partial = static_cast<long long*>(workspace);
+    ws.mean = reinterpret_cast<float*>(static_cast<char*>(workspace) + mean_off);
+    return launch_quantize(*shape, nullptr, k_f16, nullptr, nullptr, k_i8, k_scale, k_mean, ws,
+                           static_cast<hipStream_t>(stream));
+}
+
+int attn_fwd_int8_fused_q(const attn_shape* shape, const void* q_f16, const int8_t* k_i8,
+                          const float* k_scale, const void* v_f16, void* o_f16, float* lse,
+                          float* q_scale_out, const int32_t* kv_head_map, int causal,
+                          float sm_scale, void* stream) {
+    int st = check_shape(shape);
+    if (st != ATTN_OK) return st;
+    if (!q_f16 || !k_i8 || !k_scale || !v_f16 || !o_f16) return ATTN_EINVAL;
+    if (!aligned(q_f16, 16) || !aligned(k_i8, 16) || !aligned(v_f16, 16) || !aligned(o_f16, 16) ||
+        !aligned(k_scale, 4) || (lse && !aligned(lse, 4)) || (q_scale_out && !aligned(q_scale_out, 4)))
+        return ATTN_EINVAL;
+    FwdParams p;
+    std::memset(&p, 0, sizeof(p));
+    if ((st = build_map(*shape, kv_head_map, &p)) != ATTN_OK) return st;
+    if ((st = check_scale(sm_scale, shape->head_dim, &p.scale_log2)) != ATTN_OK) return st;
+    fill_common(*shape, &p);
+    p.q = q_f16;
+    p.k = k_i8;
+    p.v = v_f16;
+    p.o = o_f16;
+    p.lse = lse;
+    p.k_scale = k_scale;
+    p.q_scale_out = q_scale_out;
+    return launch_fwd(FwdKind::kInt8FusedQ, shape->head_dim, causal != 0, p, static_cast<hipStream_t>(stream));
+}
+
 int attn_fwd_int8(const attn_shape* shape, const int8_t* q_i8, const float* q_scale,
                   const int8_t* k_i8, const float* k_scale, const void* v_f16, void* o_f16,
                   float* lse, const int32_t* kv_head_map, int causal, float sm_scale,

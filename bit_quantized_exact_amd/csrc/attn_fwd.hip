@@ -139,9 +139,10 @@ __device__ __forceinline__ void score_tile(const char* ks, const typename Cfg<D,
 
 using geom::key_offset;
 
-template <int D, bool INT8, bool CAUSAL, bool DUMP>
+template <int D, bool INT8, bool CAUSAL, bool DUMP, bool QF16 = false>
 __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(const FwdParams p) {
+    static_assert(!QF16 || (INT8 && !DUMP), "in-kernel Q quantisation is an INT8 forward variant");
     using C = Cfg<D, INT8>;
     typedef typename C::qfrag_t qfrag_t;
     typedef typename C::acc_t acc_t;
@@ -172,19 +173,6 @@ void fwd_kernel(const FwdParams p) {
 
     const int nkt = geom::block_key_tiles(S, q0, CAUSAL);      // key tiles of the block
     const int nkt_w = geom::wave_key_tiles(nkt, qw0, CAUSAL);  // key tiles this wave needs
-
-    // ---- Q fragment (B operand of S^T = K Q^T), kept in VGPRs.  Rows past
-    // the sequence read the last row; they are never stored.
-    qfrag_t qf[C::QSTEPS];
-    {
-        const char* qrow = static_cast<const char*>(p.q) +
-                           (bhq * S + static_cast<size_t>(geom::q_row(qi, S))) * (D * C::KELT);
-#pragma unroll
-        for (int s = 0; s < C::QSTEPS; ++s) {
-            // 16 bytes per lane: int8 elements s*32 + g*16.., or fp16 elements s*16 + g*8..
-            qf[s] = *reinterpret_cast<const qfrag_t*>(qrow + C::q_frag_offset(s, g));
-        }
-    }
 
     // ---- K / V staging: each thread moves KPT (VPT) 16-byte chunks per tile.
     // Rows past the sequence are read from row S-1 (always in bounds) and
@@ -235,6 +223,72 @@ void fwd_kernel(const FwdParams p) {
         }
     };
 
+    // The first K tile's loads are issued before Q is read and quantised,
+    // so the two latencies overlap.
+    if constexpr (!DUMP) gload_k(0, kreg[0]);
+
+    // ---- Q fragment (B operand of S^T = K Q^T), kept in VGPRs.  Rows past
+    // the sequence read the last row; they are never stored.
+    qfrag_t qf[C::QSTEPS];
+    float qscale_fused = 0.0f;
+    if constexpr (!QF16) {
+        const char* qrow = static_cast<const char*>(p.q) +
+                           (bhq * S + static_cast<size_t>(geom::q_row(qi, S))) * (D * C::KELT);
+#pragma unroll
+        for (int s = 0; s < C::QSTEPS; ++s) {
+            // 16 bytes per lane: int8 elements s*32 + g*16.., or fp16 elements s*16 + g*8..
+            qf[s] = *reinterpret_cast<const qfrag_t*>(qrow + C::q_frag_offset(s, g));
+        }
+    } else {
+        // In-kernel per-block quantisation of Q (SageAttention article,
+        // 技术方案: INT8 Q with one scale per FlashAttention-sized block).  The
+        // workgroup's 128 rows are exactly one Q block, so the block absmax is
+        // a workgroup reduction and INT8 Q never goes through HBM.  Same rule
+        // as the standalone quantiser: a = max|x|, r = 127/a, delta = a/127
+        // (correctly rounded), q = clamp(rint(x * r), -127, 127); a == 0 gives
+        // q = 0 and delta = 0.  Rows past the sequence repeat row S-1, which
+        // leaves the maximum unchanged.
+        const char* qrow = static_cast<const char*>(p.q) +
+                           (bhq * S + static_cast<size_t>(geom::q_row(qi, S))) * (2 * D);
+        float xq[C::QSTEPS][16];
+        float amax = 0.0f;
+#pragma unroll
+        for (int s = 0; s < C::QSTEPS; ++s)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const h8 v = *reinterpret_cast<const h8*>(qrow + C::q16_piece_offset(s, g, hh));
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    xq[s][hh * 8 + e] = static_cast<float>(v[e]);
+                    amax = __builtin_fmaxf(amax, __builtin_fabsf(xq[s][hh * 8 + e]));
+                }
+            }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, off));
+        __shared__ float qmax[4];
+        if (lane == 0) qmax[wave] = amax;
+        __syncthreads();
+        const float a = __builtin_fmaxf(__builtin_fmaxf(qmax[0], qmax[1]), __builtin_fmaxf(qmax[2], qmax[3]));
+        const float r = a == 0.0f ? 0.0f : __fdiv_rn(127.0f, a);
+        qscale_fused = a == 0.0f ? 0.0f : __fdiv_rn(a, 127.0f);
+#pragma unroll
+        for (int s = 0; s < C::QSTEPS; ++s) {
+            uint32_t w[4];
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+                uint32_t packed = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float t = __builtin_rintf(xq[s][e4 * 4 + e] * r);
+                    t = __builtin_fminf(__builtin_fmaxf(t, -127.0f), 127.0f);
+                    packed |= (static_cast<uint32_t>(static_cast<int>(t)) & 0xffu) << (8 * e);
+                }
+                w[e4] = packed;
+            }
+            __builtin_memcpy(&qf[s], w, 16);
+        }
+    }
+
     // Visible keys of a tile at n0 satisfy key_offset(mt, r) < lim for this lane.
     auto mask_limit = [&](int n0) { return geom::mask_limit(n0, S, qi, g, CAUSAL); };
     auto tile_needs_mask = [&](int n0) { return (n0 + kBN > S) || (CAUSAL && n0 + kBN - 1 > qw0); };
@@ -269,12 +323,12 @@ void fwd_kernel(const FwdParams p) {
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) oacc[dt] = f16x{};
         float qscale = 1.0f;
-        if constexpr (INT8) qscale = p.q_scale[bhq * p.nqblk + qt];
+        if constexpr (INT8) qscale = QF16 ? qscale_fused : p.q_scale[bhq * p.nqblk + qt];
+        const float* kscale = p.k_scale;
 
         // ---- prologue: K_0 -> LDS, S_0, then K_1 and V_0 -> LDS (and, at
         // depth 2, K_2 and V_1 into the second register set) ----
         acc_t sc[2];
-        gload_k(0, kreg[0]);
         sstore_k(0, kreg[0]);
         __syncthreads();
         score_tile<D, INT8>(kbuf(0), qf, l32, g, sc);
@@ -303,7 +357,7 @@ void fwd_kernel(const FwdParams p) {
             if (j < nkt_w) {
                 // scores in log2 units: s * c with c = (dQ dK) sm_scale log2(e)
                 float c = p.scale_log2;
-                if constexpr (INT8) c = fmaxf(qscale * p.k_scale[bhk * p.nkblk + j] * p.scale_log2, FLT_MIN);
+                if constexpr (INT8) c = fmaxf(qscale * kscale[bhk * p.nkblk + j] * p.scale_log2, FLT_MIN);
                 float sv[2][16];
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt)
@@ -395,6 +449,10 @@ void fwd_kernel(const FwdParams p) {
             for (int j = 0; j < nkt; ++j) step(j, std::integral_constant<int, 0>{});
         }
 
+        // (stored after the loop: a global store ahead of it would keep the
+        // compiler from using scalar loads for the per-tile K scales)
+        if constexpr (QF16)
+            if (p.q_scale_out && tid == 0) p.q_scale_out[bhq * p.nqblk + qt] = qscale_fused;
         const float l_tot = row_sum(l_run);
         const float inv = 1.0f / l_tot;
         if (qi < S) {
@@ -412,10 +470,10 @@ void fwd_kernel(const FwdParams p) {
     }
 }
 
-template <int D, bool INT8, bool CAUSAL, bool DUMP>
+template <int D, bool INT8, bool CAUSAL, bool DUMP, bool QF16 = false>
 void launch_one(const FwdParams& p, hipStream_t st) {
     const int blocks = p.B * p.Hq * p.ntiles;
-    hipLaunchKernelGGL((fwd_kernel<D, INT8, CAUSAL, DUMP>), dim3(blocks), dim3(kFwdThreads), 0, st, p);
+    hipLaunchKernelGGL((fwd_kernel<D, INT8, CAUSAL, DUMP, QF16>), dim3(blocks), dim3(kFwdThreads), 0, st, p);
 }
 
 template <int D>
@@ -429,6 +487,9 @@ void launch_d(FwdKind kind, bool causal, const FwdParams& p, hipStream_t st) {
             break;
         case FwdKind::kDumpInt8:
             causal ? launch_one<D, true, true, true>(p, st) : launch_one<D, true, false, true>(p, st);
+            break;
+        case FwdKind::kInt8FusedQ:
+            causal ? launch_one<D, true, true, false, true>(p, st) : launch_one<D, true, false, false, true>(p, st);
             break;
     }
 }

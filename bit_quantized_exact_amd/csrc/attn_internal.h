@@ -35,6 +35,7 @@ struct QuantWorkspace {
 // Offsets of the workspace pieces for a shape (256-byte aligned pieces).
 size_t quant_workspace_layout(const attn_shape& s, size_t* mean_offset, int* nchunk);
 
+// q may be null (K only): then q_i8 and q_scale are not touched.
 int launch_quantize(const attn_shape& s, const void* q, const void* k, int8_t* q_i8,
                     float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
                     const QuantWorkspace& ws, hipStream_t st);
@@ -48,6 +49,7 @@ struct FwdParams {
     const float* q_scale; // int8 path: [B,Hq,nqblk]
     const float* k_scale; // int8 path: [B,Hkv,nkblk]
     int32_t* s_out;       // score dump: [B,Hq,ntiles*BM,S]
+    float* q_scale_out;   // fused-Q INT8 path: the Q block scales, [B,Hq,nqblk], or null
     int B, Hq, Hkv, S;
     int nqt;              // query tiles in the sequence
     int nqblk, nkblk;     // scale blocks per (b, head)
@@ -57,7 +59,7 @@ struct FwdParams {
     uint8_t horder[ATTN_MAX_HEADS];  // q-heads ordered by kv-head (launch order)
 };
 
-enum class FwdKind { kFp16, kInt8, kDumpInt8 };
+enum class FwdKind { kFp16, kInt8, kDumpInt8, kInt8FusedQ };
 
 int launch_fwd(FwdKind kind, int head_dim, bool causal, const FwdParams& p, hipStream_t st);
 

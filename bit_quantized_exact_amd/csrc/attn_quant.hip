@@ -200,9 +200,10 @@ int launch_quantize_d(const attn_shape& s, const void* q, const void* k, int8_t*
     const int nkb = ceil_div(S, kBK), nqb = ceil_div(S, kBQ);
     hipLaunchKernelGGL((quant_block_kernel<D, kBK, true>), dim3(nkb, s.heads_kv, s.batch),
                        dim3(256), 0, st, kk, ws.mean, k_i8, k_scale, s.heads_kv, S, nkb);
-    hipLaunchKernelGGL((quant_block_kernel<D, kBQ, false>), dim3(nqb, s.heads_q, s.batch),
-                       dim3(256), 0, st, qq, static_cast<const float*>(nullptr), q_i8, q_scale,
-                       s.heads_q, S, nqb);
+    if (qq)
+        hipLaunchKernelGGL((quant_block_kernel<D, kBQ, false>), dim3(nqb, s.heads_q, s.batch),
+                           dim3(256), 0, st, qq, static_cast<const float*>(nullptr), q_i8, q_scale,
+                           s.heads_q, S, nqb);
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ELAUNCH;
 }
 

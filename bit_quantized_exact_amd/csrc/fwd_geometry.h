@@ -81,6 +81,12 @@ struct Stage {
     __host__ __device__ static constexpr int q_frag_offset(int s, int g) {
         return INT8 ? (s * 32 + g * 16) : (s * 16 + g * 8) * 2;
     }
+    // fused Q quantisation (INT8 path reading fp16 Q): byte offset within an
+    // fp16 Q row of 16-byte piece h (0, 1) of the 16 elements behind the
+    // int8 fragment of k-step s, lane half g
+    __host__ __device__ static constexpr int q16_piece_offset(int s, int g, int h) {
+        return (s * 32 + g * 16 + h * 8) * 2;
+    }
 };
 
 // Score register r of 32-key sub-tile mt (32x32 MFMA accumulator layout)

@@ -125,6 +125,27 @@ int attn_fwd_int8(const attn_shape* shape, const int8_t* q_i8, const float* q_sc
                   void* o_f16, float* lse, const int32_t* kv_head_map, int causal,
                   float sm_scale, void* stream);
 
+/* K smoothing and per-block INT8 quantisation of K only: the K half of
+ * attn_quantize_qk (same outputs, same rules, same workspace size), for use
+ * with attn_fwd_int8_fused_q. */
+int attn_quantize_k(const attn_shape* shape, const void* k_f16, int8_t* k_i8, float* k_scale,
+                    float* k_mean, void* workspace, void* stream);
+
+/* 8-bit attention forward that quantises Q itself: Q is read as fp16 and
+ * each BQ-row block is quantised inside the forward kernel with exactly the
+ * rule of attn_quantize_qk (the kernel's query tile is one Q block), so INT8
+ * Q never travels through HBM.  Otherwise identical to attn_fwd_int8: for the
+ * same inputs it returns bitwise the same O and lse as attn_quantize_qk
+ * followed by attn_fwd_int8.
+ * q_f16 in fp16 [B,Hq,S,D]; k_i8, k_scale from attn_quantize_k (or
+ * attn_quantize_qk); v_f16 fp16 [B,Hkv,S,D]; o_f16 out fp16 [B,Hq,S,D];
+ * lse out fp32 [B,Hq,S] or NULL; q_scale_out out fp32 [B,Hq,ceil(S/BQ)] (the
+ * Q block scales) or NULL. */
+int attn_fwd_int8_fused_q(const attn_shape* shape, const void* q_f16, const int8_t* k_i8,
+                          const float* k_scale, const void* v_f16, void* o_f16, float* lse,
+                          float* q_scale_out, const int32_t* kv_head_map, int causal,
+                          float sm_scale, void* stream);
+
 /* Exact FP16 attention forward (the FlashAttention-style baseline,
  * [FA-guide]: exact values, tiles in on-chip memory, online softmax).
  *   s = (Q K^T) * sm_scale with FP16 MFMA and fp32 accumulation, online

@@ -70,6 +70,11 @@ static void check_shape(int B, int Hq, int S, bool causal, bool dump, int tile_l
                 for (int s = 0; s < St::QSTEPS; ++s) {
                     const int off = St::q_frag_offset(s, g);
                     REQUIRE(off >= 0 && off + 16 <= St::KROWG, "q frag offset %d", off);
+                    if (INT8)
+                        for (int hh = 0; hh < 2; ++hh) {
+                            const int o16 = St::q16_piece_offset(s, g, hh);
+                            REQUIRE(o16 >= 0 && o16 + 16 <= 2 * D, "fp16 q piece offset %d", o16);
+                        }
                 }
                 if (!dump && qi < S)
                     for (int dt = 0; dt < D / 32; ++dt)

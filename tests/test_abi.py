@@ -163,3 +163,33 @@ def test_python_binding_rejects_cpu_tensors():
         A.fwd_fp16(q, q, q)
     with pytest.raises(ValueError):
         A.quantize_qk(q, q)
+
+
+def test_quantize_k_validation():
+    L = A.lib()
+    sh = _sh()
+    assert L.attn_quantize_k(None, FAKE, FAKE, FAKE, None, FAKE, None) == -1
+    for args in [(None, FAKE, FAKE, None, FAKE), (FAKE, None, FAKE, None, FAKE),
+                 (FAKE, FAKE, None, None, FAKE), (FAKE, FAKE, FAKE, None, None),
+                 (MISALIGNED, FAKE, FAKE, None, FAKE), (FAKE, FAKE, FAKE + 2, None, FAKE)]:
+        assert L.attn_quantize_k(ctypes.byref(sh), *args, None) == -1
+    bad = _sh(D=96)
+    assert L.attn_quantize_k(ctypes.byref(bad), FAKE, FAKE, FAKE, None, FAKE, None) == -2
+
+
+def test_fused_q_validation():
+    L = A.lib()
+    sh = _sh()
+
+    def call(q=FAKE, k=FAKE, ks=FAKE, v=FAKE, o=FAKE, lse=None, qs=None, mp=None, scale=0.0, shape=sh):
+        return L.attn_fwd_int8_fused_q(ctypes.byref(shape) if shape is not None else None, q, k, ks,
+                                       v, o, lse, qs, mp, 0, scale, None)
+    assert call(shape=None) == -1
+    for arg in ("q", "k", "ks", "v", "o"):
+        assert call(**{arg: None}) == -1
+    assert call(q=MISALIGNED) == -1
+    assert call(qs=FAKE + 2) == -1
+    assert call(scale=float("nan")) == -1
+    assert call(shape=_sh(Hq=6, Hkv=4)) == -1
+    bad = (ctypes.c_int32 * 4)(0, 1, 2, 0)
+    assert call(mp=ctypes.cast(bad, ctypes.c_void_p)) == -4

@@ -261,3 +261,43 @@ def test_custom_scale_and_sageattn_wrapper():
     assert torch.equal(s, t)
     cos, rel = cos_rel_l1(host(s), O.attention(q, k, v, causal=True, sm_scale=0.1))
     assert cos >= INT8_COS_MIN and rel <= INT8_REL_L1_MAX
+
+
+# --------------------------------------------------------------------------
+# fused Q quantisation: bitwise the same as quantize_qk + fwd_int8
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("S,D,Hq,Hkv,causal", [
+    (1, 64, 2, 2, False), (17, 128, 4, 2, True), (127, 64, 3, 3, True), (128, 128, 4, 1, False),
+    (129, 128, 8, 2, True), (300, 64, 2, 1, False), (1000, 128, 4, 2, True)])
+def test_fused_q_matches_two_call_path_bitwise(S, D, Hq, Hkv, causal):
+    w = small_workload(1, Hq, Hkv, S, D, causal, seed=5000 + S + D)
+    q, k, v = make_qkv(w)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    case(f"fused-q S={S} D={D} Hq={Hq} Hkv={Hkv} causal={causal}")
+    qz = A.quantize_qk(qd, kd)
+    o_ref, lse_ref = A.fwd_int8(qz, vd, causal=causal, return_lse=True)
+    kz = A.quantize_k(kd)
+    qs = torch.full_like(qz["q_scale"], -1.0)
+    o, lse = A.fwd_int8_fused_q(qd, kz, vd, causal=causal, return_lse=True, q_scale_out=qs)
+    torch.cuda.synchronize()
+    for key in ("k_i8", "k_scale", "k_mean"):
+        assert torch.equal(kz[key], qz[key]), key
+    assert torch.equal(qs, qz["q_scale"])
+    assert torch.equal(o, o_ref)
+    assert torch.equal(lse, lse_ref)
+
+
+@pytest.mark.parametrize("name", ["llm_prefill_gqa", "batched_mqa", "video_mha"])
+def test_fused_q_workloads_bitwise_and_accuracy(name):
+    w = WORKLOADS[name]
+    q, k, v = make_qkv(w)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    case(f"fused-q workload {name}")
+    qz = A.quantize_qk(qd, kd)
+    o_ref = A.fwd_int8(qz, vd, causal=w.causal)
+    o = A.sageattn(qd, kd, vd, is_causal=w.causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref)
+    rows = sample_rows(w.seq, 16, seed=w.seed + 7)
+    cos, rel = cos_rel_l1(host(o)[:, :, rows], O.attention(q, k, v, causal=w.causal, rows=rows))
+    assert cos >= INT8_COS_MIN and rel <= INT8_REL_L1_MAX, (cos, rel)
