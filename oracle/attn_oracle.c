@@ -6,7 +6,10 @@
  * header, table or helper with the HIP path under bit_quantized_exact_amd/.
  *
  * It is deliberately plain and slow: fp64 loops, two-pass softmax, no tiling,
- * no online rescaling, no blocking beyond what the definitions state.
+ * no online rescaling, no blocking beyond what the definitions state.  The one
+ * exception is O5, the 8-bit P.V model: there the rounding of each weight is
+ * defined relative to the online softmax's running maximum, so O5 follows the
+ * online algorithm over key tiles, step by step as the pages describe it.
  *
  * Sources (web pages; cited by title and section):
  *   [MHA-GQA]  "注意力即一切：从 MHA 到 GQA" (bojinhu.xyz):
@@ -34,6 +37,11 @@
  *   - Causal means key j is visible to query i iff j <= i (one sequence length).
  *   - A row with no visible key (cannot happen for square causal) gives O = 0
  *     and lse = -inf.
+ *   - FP8 means OCP E4M3 (bias 7, max 448, no infinities).  FP8 Q/K blocks use
+ *     the INT8 rule with 448 in place of 127 and E4M3 rounding (nearest, ties
+ *     to even) in place of rint + clamp.  8-bit P is E4M3(448 p) / 448 with p
+ *     <= 1 taken against the running maximum; 8-bit V has one E4M3 scale per
+ *     (batch, kv-head, channel) over all tokens.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fno-fast-math -shared -fPIC.
  */
@@ -380,6 +388,280 @@ int oracle_quant_attention(int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_
         free(s); free(acc);
     }
     free(V);
+    return status;
+}
+
+/* ------------------------------------------------------------------------ */
+/* FP8 E4M3 (the OCP "e4m3fn" format) from its definition: 1 sign bit, 4    */
+/* exponent bits with bias 7, 3 fraction bits; exponent 0 is subnormal      */
+/* (f * 2^-9); there is no infinity and S.1111.111 is NaN, so the largest   */
+/* finite magnitude is 1.75 * 2^8 = 448.  Used for the FP8 alternative that */
+/* the SageAttention article compares INT8 with ([SA] 技术方案: INT8 Q/K is */
+/* more accurate than FP8; 8-bit P and V lose accuracy in some layers).     */
+/* ------------------------------------------------------------------------ */
+double oracle_e4m3_decode(uint8_t c)
+{
+    int sign = (c >> 7) & 1;
+    int expo = (c >> 3) & 0xf;
+    int frac = c & 7;
+    double v;
+    if (expo == 15 && frac == 7) return NAN;
+    if (expo == 0) v = ldexp((double)frac, -9);
+    else v = ldexp((double)(8 + frac), expo - 10);      /* 1.fff * 2^(e-7) */
+    return sign ? -v : v;
+}
+
+/* Nearest E4M3 value of x (ties to even); magnitudes that round beyond 448
+ * saturate to 448.  The sign of x is kept (a negative x that rounds to zero
+ * gives -0). */
+double oracle_e4m3_round(double x)
+{
+    if (x == 0.0 || isnan(x)) return x;
+    double ax = fabs(x);
+    int e;
+    frexp(ax, &e);                  /* ax = m * 2^e, m in [0.5, 1) */
+    int ulp_exp = (e - 1) - 3;      /* 4 significant bits in the normal range */
+    if (ulp_exp < -9) ulp_exp = -9; /* subnormal spacing 2^-9 */
+    double r = ldexp(rint(ldexp(ax, -ulp_exp)), ulp_exp);
+    if (r > 448.0) r = 448.0;
+    return signbit(x) ? -r : r;
+}
+
+/* Code of an E4M3 value (x must lie on the grid, |x| <= 448). */
+uint8_t oracle_e4m3_encode(double x)
+{
+    uint8_t sign = signbit(x) ? 0x80 : 0;
+    double ax = fabs(x);
+    if (ax == 0.0) return sign;
+    if (ax < ldexp(1.0, -6)) return sign | (uint8_t)(ax * 512.0);   /* subnormal: f * 2^-9 */
+    int e;
+    double m = frexp(ax, &e);       /* ax = m * 2^e, m in [0.5, 1) -> 1.fff * 2^(e-1) */
+    int expo = e - 1 + 7;
+    int frac = (int)((m * 2.0 - 1.0) * 8.0);
+    return sign | (uint8_t)(expo << 3) | (uint8_t)frac;
+}
+
+void oracle_e4m3_round_array(const double* x, double* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_round(x[i]);
+}
+
+void oracle_e4m3_decode_array(const uint8_t* c, double* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_decode(c[i]);
+}
+
+/* O3 with an E4M3 grid instead of the INT8 one (the FP8 alternative): per */
+/* block a = max|x|, r = 448/a (fp32, RNE), t = clamp(x*r, -448, 448) in    */
+/* fp32, code = E4M3(t) (nearest, ties to even), delta = a/448.  a == 0     */
+/* gives r = 0, codes of +-0 and delta = 0.                                 */
+void oracle_quant_blocks_e4m3(int64_t nmat, int32_t S, int32_t D, int32_t block,
+                              const float* x, uint8_t* q, float* scale)
+{
+    int32_t nblk = (S + block - 1) / block;
+    for (int64_t mtx = 0; mtx < nmat; ++mtx) {
+        for (int32_t bi = 0; bi < nblk; ++bi) {
+            int32_t r0 = bi * block, r1 = r0 + block < S ? r0 + block : S;
+            const float* xb = x + (mtx * S + r0) * D;
+            uint8_t* qb = q + (mtx * S + r0) * D;
+            int64_t n = (int64_t)(r1 - r0) * D;
+            float a = 0.0f;
+            for (int64_t e = 0; e < n; ++e) {
+                float v = fabsf(xb[e]);
+                if (v > a) a = v;
+            }
+            float r = a == 0.0f ? 0.0f : 448.0f / a;
+            for (int64_t e = 0; e < n; ++e) {
+                float t = xb[e] * r;
+                if (t > 448.0f) t = 448.0f;
+                if (t < -448.0f) t = -448.0f;
+                qb[e] = oracle_e4m3_encode(oracle_e4m3_round((double)t));
+            }
+            scale[mtx * nblk + bi] = a == 0.0f ? 0.0f : a / 448.0f;
+        }
+    }
+}
+
+/* 8-bit V of the P.V ablation: one E4M3 scale per (batch, kv-head, channel) */
+/* over all tokens, a_c = max_j |V[j,c]|, r = 448/a_c, code = E4M3(clamp(   */
+/* v*r)), delta_c = a_c/448.  codes: [B,Hkv,S,D]; scale: [B,Hkv,D].          */
+void oracle_quant_v_e4m3(int32_t B, int32_t Hkv, int32_t S, int32_t D,
+                         const uint16_t* v_f16, uint8_t* codes, float* scale)
+{
+    for (int64_t bk = 0; bk < (int64_t)B * Hkv; ++bk) {
+        const uint16_t* Vh = v_f16 + bk * S * D;
+        for (int c = 0; c < D; ++c) {
+            float a = 0.0f;
+            for (int32_t j = 0; j < S; ++j) {
+                float v = fabsf((float)oracle_half_to_double(Vh[(int64_t)j * D + c]));
+                if (v > a) a = v;
+            }
+            float r = a == 0.0f ? 0.0f : 448.0f / a;
+            for (int32_t j = 0; j < S; ++j) {
+                float t = (float)oracle_half_to_double(Vh[(int64_t)j * D + c]) * r;
+                if (t > 448.0f) t = 448.0f;
+                if (t < -448.0f) t = -448.0f;
+                codes[(bk * S + j) * D + c] = oracle_e4m3_encode(oracle_e4m3_round((double)t));
+            }
+            scale[bk * D + c] = a == 0.0f ? 0.0f : a / 448.0f;
+        }
+    }
+}
+
+/* O4 on E4M3 codes: the same quantised-attention model as                 */
+/* oracle_quant_attention, with scores sum_c dec(q) dec(k) (exact in fp64:  */
+/* every product of two E4M3 values has at most 8 significant bits).       */
+int oracle_quant_attention_e4m3(int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t D,
+                                const uint8_t* q_f8, const float* q_scale, int32_t bq,
+                                const uint8_t* k_f8, const float* k_scale, int32_t bk,
+                                const uint16_t* v_f16, const int32_t* kv_map,
+                                int32_t causal, double sm_scale, int32_t l_from_rounded,
+                                const int32_t* rows, int32_t nrows,
+                                double* out, double* lse, int32_t nthreads)
+{
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || D <= 0 || bq <= 0 || bk <= 0) return -1;
+    if (check_map(Hq, Hkv, kv_map)) return -4;
+    if (!rows) nrows = S;
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+    int32_t nbq = (S + bq - 1) / bq, nbk = (S + bk - 1) / bk;
+    int64_t nkv = (int64_t)B * Hkv * S * D;
+    double* V = decode_all(v_f16, nkv);
+    double* Kd = (double*)malloc((size_t)nkv * sizeof(double));
+    if (!V || !Kd) { free(V); free(Kd); return -5; }
+    oracle_e4m3_decode_array(k_f8, Kd, nkv);
+    int64_t total = (int64_t)B * Hq * nrows;
+    int status = 0;
+#pragma omp parallel
+    {
+        double* s = (double*)malloc((size_t)S * sizeof(double));
+        double* acc = (double*)malloc((size_t)D * sizeof(double));
+        double* qrow = (double*)malloc((size_t)D * sizeof(double));
+        if (!s || !acc || !qrow) {
+#pragma omp atomic write
+            status = -5;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t t = 0; t < total; ++t) {
+                int64_t bh = t / nrows;
+                int32_t r = (int32_t)(t % nrows);
+                int32_t i = rows ? rows[r] : r;
+                int32_t b = (int32_t)(bh / Hq), h = (int32_t)(bh % Hq);
+                int32_t kh = kv_map[h];
+                const uint8_t* qp = q_f8 + (((int64_t)b * Hq + h) * S + i) * D;
+                const double* Kh = Kd + ((int64_t)b * Hkv + kh) * S * D;
+                const double* Vh = V + ((int64_t)b * Hkv + kh) * S * D;
+                double dq = (double)q_scale[((int64_t)b * Hq + h) * nbq + i / bq];
+                const float* dk = k_scale + ((int64_t)b * Hkv + kh) * nbk;
+                double* o = out + t * D;
+                for (int c = 0; c < D; ++c) qrow[c] = oracle_e4m3_decode(qp[c]);
+                int32_t nvis = causal ? (i + 1 < S ? i + 1 : S) : S;
+                double m = -INFINITY;
+                for (int32_t j = 0; j < nvis; ++j) {
+                    double dot = 0.0;
+                    for (int c = 0; c < D; ++c) dot += qrow[c] * Kh[(int64_t)j * D + c];
+                    s[j] = dot * dq * (double)dk[j / bk] * sm_scale;
+                    if (s[j] > m) m = s[j];
+                }
+                double l = 0.0;
+                for (int c = 0; c < D; ++c) acc[c] = 0.0;
+                for (int32_t j = 0; j < nvis; ++j) {
+                    double p = exp(s[j] - m);
+                    double pr = oracle_round_to_half(p);
+                    l += l_from_rounded ? pr : p;
+                    for (int c = 0; c < D; ++c) acc[c] += pr * Vh[(int64_t)j * D + c];
+                }
+                for (int c = 0; c < D; ++c) o[c] = acc[c] / l;
+                if (lse) lse[t] = m + log(l);
+            }
+        }
+        free(s); free(acc); free(qrow);
+    }
+    free(V); free(Kd);
+    return status;
+}
+
+/* ------------------------------------------------------------------------ */
+/* O5: the 8-bit P.V ablation ([SA] 技术方案 reports that 8-bit P and V     */
+/* fail in some layers).  Scores as O4 (INT8 Q/K).  The weights are        */
+/* quantised inside the online softmax ("FlashAttention" guide, FAQ;       */
+/* [MHA-GQA] §8.2): keys arrive in tiles of `tile` keys; for each tile     */
+/*   m_t = max(m_{t-1}, max_j s_j),  alpha = exp(m_{t-1} - m_t),            */
+/*   p_j = exp(s_j - m_t),  l_t = alpha l_{t-1} + sum_j p_j,                */
+/*   acc_t = alpha acc_{t-1} + sum_j (E4M3(448 p_j) / 448) V'_j,            */
+/* where V'_j = dec(v_code[j,c]) * delta_c, and O = acc / l.  The weight of */
+/* a key is therefore rounded relative to the running maximum at its tile. */
+/* p_quant = 0 keeps p unrounded (then O equals exact attention on the     */
+/* same scores and V').  v_codes: [B,Hkv,S,D]; v_scale: [B,Hkv,D].         */
+/* ------------------------------------------------------------------------ */
+int oracle_pv8_attention(int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t D,
+                         const int8_t* q_i8, const float* q_scale, int32_t bq,
+                         const int8_t* k_i8, const float* k_scale, int32_t bk,
+                         const uint8_t* v_codes, const float* v_scale, const int32_t* kv_map,
+                         int32_t causal, double sm_scale, int32_t tile, int32_t p_quant,
+                         const int32_t* rows, int32_t nrows,
+                         double* out, double* lse, int32_t nthreads)
+{
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || D <= 0 || bq <= 0 || bk <= 0 || tile <= 0)
+        return -1;
+    if (check_map(Hq, Hkv, kv_map)) return -4;
+    if (!rows) nrows = S;
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+    int32_t nbq = (S + bq - 1) / bq, nbk = (S + bk - 1) / bk;
+    int64_t total = (int64_t)B * Hq * nrows;
+    int status = 0;
+#pragma omp parallel
+    {
+        double* s = (double*)malloc((size_t)S * sizeof(double));
+        double* acc = (double*)malloc((size_t)D * sizeof(double));
+        if (!s || !acc) {
+#pragma omp atomic write
+            status = -5;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t t = 0; t < total; ++t) {
+                int64_t bh = t / nrows;
+                int32_t r = (int32_t)(t % nrows);
+                int32_t i = rows ? rows[r] : r;
+                int32_t b = (int32_t)(bh / Hq), h = (int32_t)(bh % Hq);
+                int32_t kh = kv_map[h];
+                const int8_t* qp = q_i8 + (((int64_t)b * Hq + h) * S + i) * D;
+                const int8_t* Kh = k_i8 + ((int64_t)b * Hkv + kh) * S * D;
+                const uint8_t* Vc = v_codes + ((int64_t)b * Hkv + kh) * S * D;
+                const float* dv = v_scale + ((int64_t)b * Hkv + kh) * D;
+                double dq = (double)q_scale[((int64_t)b * Hq + h) * nbq + i / bq];
+                const float* dk = k_scale + ((int64_t)b * Hkv + kh) * nbk;
+                double* o = out + t * D;
+                int32_t nvis = causal ? (i + 1 < S ? i + 1 : S) : S;
+                for (int32_t j = 0; j < nvis; ++j) {
+                    int64_t dot = 0;
+                    for (int c = 0; c < D; ++c) dot += (int64_t)qp[c] * (int64_t)Kh[(int64_t)j * D + c];
+                    s[j] = (double)dot * dq * (double)dk[j / bk] * sm_scale;
+                }
+                double m = -INFINITY, l = 0.0;
+                for (int c = 0; c < D; ++c) acc[c] = 0.0;
+                for (int32_t j0 = 0; j0 < nvis; j0 += tile) {
+                    int32_t j1 = j0 + tile < nvis ? j0 + tile : nvis;
+                    double mt = m;
+                    for (int32_t j = j0; j < j1; ++j)
+                        if (s[j] > mt) mt = s[j];
+                    double alpha = exp(m - mt);     /* exp(-inf) = 0 on the first tile */
+                    l *= alpha;
+                    for (int c = 0; c < D; ++c) acc[c] *= alpha;
+                    for (int32_t j = j0; j < j1; ++j) {
+                        double p = exp(s[j] - mt);
+                        l += p;
+                        double pq = p_quant ? oracle_e4m3_round(p * 448.0) / 448.0 : p;
+                        for (int c = 0; c < D; ++c)
+                            acc[c] += pq * (oracle_e4m3_decode(Vc[(int64_t)j * D + c]) * (double)dv[c]);
+                    }
+                    m = mt;
+                }
+                for (int c = 0; c < D; ++c) o[c] = acc[c] / l;
+                if (lse) lse[t] = m + log(l);
+            }
+        }
+        free(s); free(acc);
+    }
     return status;
 }
 

@@ -63,6 +63,21 @@ def lib():
                                              P, I32, P, P, I32])
         L.oracle_quant_attention.restype = ctypes.c_int
         L.oracle_max_threads.restype = ctypes.c_int
+        L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3_decode.restype = D
+        L.oracle_e4m3_round.argtypes = [D]
+        L.oracle_e4m3_round.restype = D
+        L.oracle_e4m3_encode.argtypes = [D]
+        L.oracle_e4m3_encode.restype = ctypes.c_uint8
+        L.oracle_e4m3_round_array.argtypes = [P, P, I64]
+        L.oracle_e4m3_decode_array.argtypes = [P, P, I64]
+        L.oracle_quant_blocks_e4m3.argtypes = [I64, I32, I32, I32, P, P, P]
+        L.oracle_quant_v_e4m3.argtypes = [I32] * 4 + [P, P, P]
+        L.oracle_quant_attention_e4m3.argtypes = L.oracle_quant_attention.argtypes
+        L.oracle_quant_attention_e4m3.restype = ctypes.c_int
+        L.oracle_pv8_attention.argtypes = ([I32] * 5 + [P, P, I32, P, P, I32, P, P, P, I32, D, I32,
+                                           I32, P, I32, P, P, I32])
+        L.oracle_pv8_attention.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -214,6 +229,115 @@ def quant_attention(qz, v, causal=False, kv_map=None, sm_scale=None, rows=None,
                                       _ptr(r) if r is not None else None, nr,
                                       _ptr(out), _ptr(lse) if lse is not None else None, int(nthreads))
     _check(st, "quant_attention")
+    return (out, lse) if with_lse else out
+
+
+# --------------------------------------------------------------------------
+# FP8 (E4M3) alternative and the 8-bit P.V ablation
+# --------------------------------------------------------------------------
+def e4m3_round(x) -> np.ndarray:
+    """Nearest E4M3 values (ties to even, saturating at 448), as fp64."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    out = np.empty_like(x)
+    lib().oracle_e4m3_round_array(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    c = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8))
+    out = np.empty(c.shape, dtype=np.float64)
+    lib().oracle_e4m3_decode_array(_ptr(c), _ptr(out), c.size)
+    return out
+
+
+def e4m3_encode(x: float) -> int:
+    return int(lib().oracle_e4m3_encode(float(x)))
+
+
+def quant_blocks_e4m3(x32, block):
+    """O3 on the E4M3 grid: returns (uint8 codes same shape, scale [..., nblk])."""
+    x32 = np.ascontiguousarray(x32, dtype=np.float32)
+    *lead, S, D = x32.shape
+    nmat = int(np.prod(lead)) if lead else 1
+    nblk = (S + block - 1) // block
+    q = np.empty(x32.shape, dtype=np.uint8)
+    sc = np.empty((*lead, nblk), dtype=np.float32)
+    lib().oracle_quant_blocks_e4m3(nmat, S, D, block, _ptr(x32), _ptr(q), _ptr(sc))
+    return q, sc
+
+
+def quantize_qk_fp8(q, k, bq=BQ, bk=BK):
+    """O2 + O3 (E4M3): returns dict with q_f8, q_scale, k_f8, k_scale, k_mean."""
+    mu = k_mean(k)
+    ks = smooth_k(k, mu)
+    qf, qs = quant_blocks_e4m3(half_to_float(q), bq)
+    kf, kscale = quant_blocks_e4m3(ks, bk)
+    return dict(q_f8=qf, q_scale=qs, k_f8=kf, k_scale=kscale, k_mean=mu)
+
+
+def quant_v_fp8(v):
+    """8-bit V of the P.V ablation: codes [B,Hkv,S,D] uint8, scale [B,Hkv,D]."""
+    B, Hkv, S, D = v.shape
+    codes = np.empty(v.shape, dtype=np.uint8)
+    sc = np.empty((B, Hkv, D), dtype=np.float32)
+    vb = _bits(v)
+    lib().oracle_quant_v_e4m3(B, Hkv, S, D, _ptr(vb), _ptr(codes), _ptr(sc))
+    return codes, sc
+
+
+def quant_attention_fp8(qz, v, causal=False, kv_map=None, sm_scale=None, rows=None,
+                        with_lse=False, bq=BQ, bk=BK, l_from_rounded=False, nthreads=0):
+    """O4 on E4M3 Q/K codes (qz from quantize_qk_fp8)."""
+    qf = np.ascontiguousarray(qz["q_f8"], dtype=np.uint8)
+    kf = np.ascontiguousarray(qz["k_f8"], dtype=np.uint8)
+    qs = np.ascontiguousarray(qz["q_scale"], dtype=np.float32)
+    ks = np.ascontiguousarray(qz["k_scale"], dtype=np.float32)
+    B, Hq, S, D = qf.shape
+    Hkv = kf.shape[1]
+    m = _map(Hq, Hkv, kv_map)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    r, nr = _rows(rows)
+    n = nr if r is not None else S
+    out = np.empty((B, Hq, n, D), dtype=np.float64)
+    lse = np.empty((B, Hq, n), dtype=np.float64) if with_lse else None
+    vb = _bits(v)
+    st = lib().oracle_quant_attention_e4m3(B, Hq, Hkv, S, D, _ptr(qf), _ptr(qs), bq, _ptr(kf),
+                                           _ptr(ks), bk, _ptr(vb), _ptr(m), int(bool(causal)),
+                                           float(sm_scale), int(bool(l_from_rounded)),
+                                           _ptr(r) if r is not None else None, nr,
+                                           _ptr(out), _ptr(lse) if lse is not None else None,
+                                           int(nthreads))
+    _check(st, "quant_attention_e4m3")
+    return (out, lse) if with_lse else out
+
+
+def pv8_attention(qz, v_codes, v_scale, causal=False, kv_map=None, sm_scale=None, rows=None,
+                  with_lse=False, bq=BQ, bk=BK, tile=BK, p_quant=True, nthreads=0):
+    """O5: INT8 Q/K scores, 8-bit P (against the running maximum of the
+    online softmax over key tiles of `tile` keys) and 8-bit V."""
+    qi = np.ascontiguousarray(qz["q_i8"])
+    ki = np.ascontiguousarray(qz["k_i8"])
+    qs = np.ascontiguousarray(qz["q_scale"], dtype=np.float32)
+    ks = np.ascontiguousarray(qz["k_scale"], dtype=np.float32)
+    vc = np.ascontiguousarray(v_codes, dtype=np.uint8)
+    vs = np.ascontiguousarray(v_scale, dtype=np.float32)
+    B, Hq, S, D = qi.shape
+    Hkv = ki.shape[1]
+    assert vc.shape == (B, Hkv, S, D) and vs.shape == (B, Hkv, D)
+    m = _map(Hq, Hkv, kv_map)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    r, nr = _rows(rows)
+    n = nr if r is not None else S
+    out = np.empty((B, Hq, n, D), dtype=np.float64)
+    lse = np.empty((B, Hq, n), dtype=np.float64) if with_lse else None
+    st = lib().oracle_pv8_attention(B, Hq, Hkv, S, D, _ptr(qi), _ptr(qs), bq, _ptr(ki), _ptr(ks), bk,
+                                    _ptr(vc), _ptr(vs), _ptr(m), int(bool(causal)), float(sm_scale),
+                                    int(tile), int(bool(p_quant)),
+                                    _ptr(r) if r is not None else None, nr,
+                                    _ptr(out), _ptr(lse) if lse is not None else None, int(nthreads))
+    _check(st, "pv8_attention")
     return (out, lse) if with_lse else out
 
 
