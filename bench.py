@@ -7,6 +7,10 @@ synthetic fp16 inputs already resident in HBM):
     attn_fwd_int8_fused_q  (per-block INT8 Q in the kernel, INT8 QK^T,
                             online softmax, FP16 P.V)
     attn_fwd_fp16          (the exact FP16 FlashAttention-style baseline)
+Outside the timed steps it also times the FP8 alternative (attn_quantize_qk_fp8
++ attn_fwd_fp8) and the 8-bit P.V ablation (attn_quantize_v_fp8 +
+attn_fwd_int8_pv8) and, with the CPU leg, reports their accuracy against the
+exact oracle on the sampled rows.
 
 Printed: ONE JSON line.  `value` is the INT8 (SageAttention-form) path's
 attention throughput, quantisation included: FLOP / (t_quantize_k +
@@ -145,6 +149,35 @@ def run_workload(name, steps, warmup, cpu=False, cpu_seconds=15.0):
     torch.cuda.synchronize()
     ms_qqk = tc[0].elapsed_time(tc[1]) / n2
     ms_8u = tc[1].elapsed_time(tc[2]) / n2
+    # the FP8 alternative (E4M3 Q/K, FP16 P.V) and the 8-bit P.V ablation
+    # (INT8 Q/K, E4M3 P and V): the comparisons the SageAttention article draws
+    of8 = torch.empty_like(qd)
+    opv8 = torch.empty_like(qd)
+    qz8 = A.quantize_qk_fp8(qd, kd, with_mean=False)
+    vz8 = A.quantize_v_fp8(vd)
+    for _ in range(max(1, warmup)):
+        A.fwd_fp8(qz8, vd, causal=w.causal, out=of8)
+        A.fwd_int8_pv8(qz, vz8, causal=w.causal, out=opv8)
+    te = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    te[0].record(stream)
+    for _ in range(n2):
+        A.quantize_qk_fp8(qd, kd, workspace=qz8["workspace"], with_mean=False)
+    te[1].record(stream)
+    for _ in range(n2):
+        A.fwd_fp8(qz8, vd, causal=w.causal, out=of8)
+    te[2].record(stream)
+    for _ in range(n2):
+        A.quantize_v_fp8(vd, workspace=vz8["workspace"])
+    te[3].record(stream)
+    for _ in range(n2):
+        A.fwd_int8_pv8(qz, vz8, causal=w.causal, out=opv8)
+    te[4].record(stream)
+    torch.cuda.synchronize()
+    ms_qf8, ms_f8, ms_qv8, ms_pv8 = (te[i].elapsed_time(te[i + 1]) / n2 for i in range(4))
+    A.quantize_qk_fp8(qd, kd, workspace=qz8["workspace"], with_mean=False)
+    A.fwd_fp8(qz8, vd, causal=w.causal, out=of8)
+    A.quantize_v_fp8(vd, workspace=vz8["workspace"])
+    A.fwd_int8_pv8(qz, vz8, causal=w.causal, out=opv8)
     A.fwd_int8_fused_q(qd, kz, vd, causal=w.causal, out=o8)   # o8 is compared below
     flop = w.flops()
     tf = lambda ms: flop / (ms * 1e-3) / 1e12
@@ -212,16 +245,26 @@ def run_workload(name, steps, warmup, cpu=False, cpu_seconds=15.0):
             "fp16": {"tflops": round(tf(ms_16), 2), "ms": round(ms_16, 4),
                      "frac_fp16_peak": round(tf(ms_16) / PEAK_TFLOPS["fp16"], 4)},
             "int8_speedup_over_fp16": round(ms_16 / (ms_q + ms_8), 3),
+            "fp8_qk": {"fwd_tflops": round(tf(ms_f8), 2), "fwd_ms": round(ms_f8, 4),
+                       "quantize_qk_fp8_ms": round(ms_qf8, 4),
+                       "two_call_tflops": round(tf(ms_qf8 + ms_f8), 2),
+                       "fwd_frac_blended_peak": round(tf(ms_f8) / PEAK_BLEND, 4),
+                       "peak_note": "fp8 QK^T at 5.0 PFLOP/s and fp16 PV at 2.5, harmonic blend"},
+            "int8_pv8": {"fwd_tflops": round(tf(ms_pv8), 2), "fwd_ms": round(ms_pv8, 4),
+                         "quantize_v_fp8_ms": round(ms_qv8, 4),
+                         "fwd_frac_peak": round(tf(ms_pv8) / PEAK_TFLOPS["int8"], 4),
+                         "peak_note": "int8 QK^T and fp8 PV, both 5.0 P(FL)OP/s"},
         },
         "roofline": {k_: (round(v_, 4) if isinstance(v_, float) else v_) for k_, v_ in roof.items()},
         "cpu_baseline": None,
     }
     if cpu:
-        rec["cpu_baseline"], rec["parity_sample"] = cpu_baseline(w, q, k, v, o8, o16, cpu_seconds)
+        rec["cpu_baseline"], rec["parity_sample"] = cpu_baseline(w, q, k, v, o8, o16, cpu_seconds,
+                                                                 extra={"fp8_qk": of8, "int8_pv8": opv8})
     return rec
 
 
-def cpu_baseline(w, q, k, v, o8, o16, target_s):
+def cpu_baseline(w, q, k, v, o8, o16, target_s, extra=None):
     """Time the CPU oracle (fp64 exact attention) on sampled query rows of the
     same workload and compare the GPU outputs on those rows."""
     from oracle import oracle as O
@@ -254,6 +297,10 @@ def cpu_baseline(w, q, k, v, o8, o16, target_s):
         "int8_cos": float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b))),
         "int8_rel_l1": float(np.abs(a - b).sum() / np.abs(b).sum()),
     }
+    for key, t in (extra or {}).items():
+        a = t.cpu().numpy()[:, :, rows].astype(np.float64).ravel()
+        parity[f"{key}_cos"] = float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b)))
+        parity[f"{key}_rel_l1"] = float(np.abs(a - b).sum() / np.abs(b).sum())
     base = {
         "value": round(fl / dt / 1e12, 6),
         "unit": "TFLOPS",

@@ -13,6 +13,10 @@ kernels.  torch provides device memory and streams.
     attn_debug_qk_int32 -> debug_qk_int32   the INT32 score tiles (test hook)
     sageattn(q, k, v, is_causal, scale)     one-call scaled_dot_product_attention
                                             replacement (quantize_k + fwd_int8_fused_q)
+    attn_quantize_qk_fp8 -> quantize_qk_fp8 the FP8 (E4M3) alternative for Q/K
+    attn_fwd_fp8     -> fwd_fp8         E4M3 QK^T, FP16 PV
+    attn_quantize_v_fp8 -> quantize_v_fp8   per-channel E4M3 V (transposed)
+    attn_fwd_int8_pv8 -> fwd_int8_pv8   INT8 QK^T with 8-bit P and V (ablation)
 
 Sources: SageAttention article ("又快又准，即插即用！清华8比特量化Attention…"),
 技术方案 and its plug-and-play example; "注意力即一切：从 MHA 到 GQA" §2.2-§5.1.
@@ -30,6 +34,7 @@ from ._native import AttnShape, lib
 __all__ = [
     "AttnError", "quant_blocks", "quantize_workspace_bytes", "quantize_qk", "quantize_k",
     "fwd_int8", "fwd_int8_fused_q", "fwd_fp16", "debug_qk_int32", "sageattn", "status_string",
+    "quantize_qk_fp8", "fwd_fp8", "v_fp8_stride", "quantize_v_fp8", "fwd_int8_pv8",
     "AttnShape", "lib",
 ]
 
@@ -265,3 +270,113 @@ def sageattn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: bool 
     kz = quantize_k(k.contiguous(), with_mean=False)
     return fwd_int8_fused_q(q.contiguous(), kz, v.contiguous(), causal=is_causal,
                             kv_head_map=kv_head_map, sm_scale=scale)
+
+
+# --------------------------------------------------------------------------
+# FP8 alternative and the 8-bit P.V ablation
+# --------------------------------------------------------------------------
+def _workspace(sh: AttnShape, workspace, dev):
+    nbytes = quantize_workspace_bytes(sh)
+    if nbytes == 0:
+        raise AttnError(_native.ATTN_EINVAL, "attn_quantize_workspace_bytes")
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    return workspace
+
+
+def quantize_qk_fp8(q: torch.Tensor, k: torch.Tensor, *, workspace: Optional[torch.Tensor] = None,
+                    with_mean: bool = True, stream=None):
+    """K smoothing + per-block E4M3 quantisation (the FP8 alternative).  Returns
+    a dict with q_f8, q_scale, k_f8, k_scale (codes as uint8), k_mean, workspace."""
+    _dev(q, torch.float16, "q")
+    _dev(k, torch.float16, "k")
+    sh = _shape(q, k)
+    bq, bk = quant_blocks()
+    B, Hq, Hkv, S, D = sh.batch, sh.heads_q, sh.heads_kv, sh.seq, sh.head_dim
+    dev = q.device
+    o = dict(q_f8=torch.empty((B, Hq, S, D), dtype=torch.uint8, device=dev),
+             q_scale=torch.empty((B, Hq, -(-S // bq)), dtype=torch.float32, device=dev),
+             k_f8=torch.empty((B, Hkv, S, D), dtype=torch.uint8, device=dev),
+             k_scale=torch.empty((B, Hkv, -(-S // bk)), dtype=torch.float32, device=dev),
+             k_mean=torch.empty((B, Hkv, D), dtype=torch.float32, device=dev) if with_mean else None)
+    o["workspace"] = _workspace(sh, workspace, dev)
+    _check(lib().attn_quantize_qk_fp8(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(o["q_f8"]),
+                                      _ptr(o["q_scale"]), _ptr(o["k_f8"]), _ptr(o["k_scale"]),
+                                      _ptr(o["k_mean"]), _ptr(o["workspace"]), _stream(stream)),
+           "attn_quantize_qk_fp8")
+    return o
+
+
+def fwd_fp8(qz: dict, v: torch.Tensor, *, causal: bool = False, kv_head_map=None,
+            sm_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+            lse: Optional[torch.Tensor] = None, return_lse: bool = False, stream=None):
+    """Attention forward on E4M3 Q/K (the output of quantize_qk_fp8), FP16 P.V."""
+    q8 = _dev(qz["q_f8"], torch.uint8, "q_f8")
+    k8 = _dev(qz["k_f8"], torch.uint8, "k_f8")
+    qs = _dev(qz["q_scale"], torch.float32, "q_scale")
+    ks = _dev(qz["k_scale"], torch.float32, "k_scale")
+    _dev(v, torch.float16, "v")
+    sh = _shape(q8, k8)
+    if tuple(v.shape) != tuple(k8.shape):
+        raise ValueError("v must have the shape of k")
+    if out is None:
+        out = torch.empty(q8.shape, dtype=torch.float16, device=v.device)
+    _dev(out, torch.float16, "out")
+    if return_lse and lse is None:
+        lse = torch.empty(q8.shape[:3], dtype=torch.float32, device=v.device)
+    _keep, mp = _map_arg(kv_head_map)
+    _check(lib().attn_fwd_fp8(ctypes.byref(sh), _ptr(q8), _ptr(qs), _ptr(k8), _ptr(ks), _ptr(v),
+                              _ptr(out), _ptr(lse), mp, int(bool(causal)), float(sm_scale or 0.0),
+                              _stream(stream)), "attn_fwd_fp8")
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def v_fp8_stride(shape: AttnShape) -> int:
+    return int(lib().attn_v_fp8_stride(ctypes.byref(shape)))
+
+
+def quantize_v_fp8(v: torch.Tensor, *, workspace: Optional[torch.Tensor] = None, stream=None):
+    """Per-channel E4M3 V for the 8-bit P.V ablation.  Returns a dict with
+    v_f8t (codes, [B, Hkv, D, stride], transposed) and v_scale [B, Hkv, D]."""
+    _dev(v, torch.float16, "v")
+    if v.dim() != 4:
+        raise ValueError("v must be [batch, heads, seq, head_dim]")
+    B, Hkv, S, D = v.shape
+    sh = AttnShape(B, Hkv, Hkv, S, D)
+    stride = v_fp8_stride(sh)
+    if stride == 0:
+        raise AttnError(_native.ATTN_EINVAL, "attn_v_fp8_stride")
+    o = dict(v_f8t=torch.empty((B, Hkv, D, stride), dtype=torch.uint8, device=v.device),
+             v_scale=torch.empty((B, Hkv, D), dtype=torch.float32, device=v.device))
+    o["workspace"] = _workspace(sh, workspace, v.device)
+    _check(lib().attn_quantize_v_fp8(ctypes.byref(sh), _ptr(v), _ptr(o["v_f8t"]), _ptr(o["v_scale"]),
+                                     _ptr(o["workspace"]), _stream(stream)), "attn_quantize_v_fp8")
+    return o
+
+
+def fwd_int8_pv8(qz: dict, vz: dict, *, causal: bool = False, kv_head_map=None,
+                 sm_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                 lse: Optional[torch.Tensor] = None, return_lse: bool = False, stream=None):
+    """INT8 Q/K (quantize_qk) with 8-bit P and V (quantize_v_fp8): the ablation."""
+    q_i8 = _dev(qz["q_i8"], torch.int8, "q_i8")
+    k_i8 = _dev(qz["k_i8"], torch.int8, "k_i8")
+    qs = _dev(qz["q_scale"], torch.float32, "q_scale")
+    ks = _dev(qz["k_scale"], torch.float32, "k_scale")
+    vt = _dev(vz["v_f8t"], torch.uint8, "v_f8t")
+    vs = _dev(vz["v_scale"], torch.float32, "v_scale")
+    sh = _shape(q_i8, k_i8)
+    stride = v_fp8_stride(sh)
+    if tuple(vt.shape) != (sh.batch, sh.heads_kv, sh.head_dim, stride):
+        raise ValueError(f"v_f8t shape {tuple(vt.shape)} does not match k")
+    if tuple(vs.shape) != (sh.batch, sh.heads_kv, sh.head_dim):
+        raise ValueError("v_scale must be [batch, heads_kv, head_dim]")
+    if out is None:
+        out = torch.empty(q_i8.shape, dtype=torch.float16, device=q_i8.device)
+    _dev(out, torch.float16, "out")
+    if return_lse and lse is None:
+        lse = torch.empty(q_i8.shape[:3], dtype=torch.float32, device=q_i8.device)
+    _keep, mp = _map_arg(kv_head_map)
+    _check(lib().attn_fwd_int8_pv8(ctypes.byref(sh), _ptr(q_i8), _ptr(qs), _ptr(k_i8), _ptr(ks),
+                                   _ptr(vt), _ptr(vs), _ptr(out), _ptr(lse), mp, int(bool(causal)),
+                                   float(sm_scale or 0.0), _stream(stream)), "attn_fwd_int8_pv8")
+    return (out, lse) if (return_lse or lse is not None) else out

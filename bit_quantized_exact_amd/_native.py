@@ -21,7 +21,8 @@ ATTN_MAX_SEQ = 1 << 22
 EXPORTED = (
     "attn_quant_blocks", "attn_quantize_workspace_bytes", "attn_quantize_qk", "attn_quantize_k",
     "attn_fwd_int8", "attn_fwd_int8_fused_q", "attn_fwd_fp16", "attn_debug_qk_int32",
-    "attn_status_string",
+    "attn_status_string", "attn_quantize_qk_fp8", "attn_fwd_fp8", "attn_v_fp8_stride",
+    "attn_quantize_v_fp8", "attn_fwd_int8_pv8",
 )
 
 
@@ -62,6 +63,16 @@ def lib():
     L.attn_fwd_fp16.restype = ctypes.c_int
     L.attn_debug_qk_int32.argtypes = [SP, P, P, P, ctypes.c_int, I32, I32, P, P]
     L.attn_debug_qk_int32.restype = ctypes.c_int
+    L.attn_quantize_qk_fp8.argtypes = [SP, P, P, P, P, P, P, P, P, P]
+    L.attn_quantize_qk_fp8.restype = ctypes.c_int
+    L.attn_fwd_fp8.argtypes = [SP, P, P, P, P, P, P, P, P, ctypes.c_int, F32, P]
+    L.attn_fwd_fp8.restype = ctypes.c_int
+    L.attn_v_fp8_stride.argtypes = [SP]
+    L.attn_v_fp8_stride.restype = ctypes.c_int64
+    L.attn_quantize_v_fp8.argtypes = [SP, P, P, P, P, P]
+    L.attn_quantize_v_fp8.restype = ctypes.c_int
+    L.attn_fwd_int8_pv8.argtypes = [SP, P, P, P, P, P, P, P, P, P, ctypes.c_int, F32, P]
+    L.attn_fwd_int8_pv8.restype = ctypes.c_int
     L.attn_status_string.argtypes = [ctypes.c_int]
     L.attn_status_string.restype = ctypes.c_char_p
     _lib = L

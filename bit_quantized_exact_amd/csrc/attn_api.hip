@@ -217,6 +217,96 @@ int attn_debug_qk_int32(const attn_shape* shape, const int8_t* q_i8, const int8_
     return launch_fwd(FwdKind::kDumpInt8, shape->head_dim, causal != 0, p, static_cast<hipStream_t>(stream));
 }
 
+int attn_quantize_qk_fp8(const attn_shape* shape, const void* q_f16, const void* k_f16,
+                         uint8_t* q_f8, float* q_scale, uint8_t* k_f8, float* k_scale,
+                         float* k_mean, void* workspace, void* stream) {
+    int st = check_shape(shape);
+    if (st != ATTN_OK) return st;
+    if (!q_f16 || !k_f16 || !q_f8 || !q_scale || !k_f8 || !k_scale || !workspace) return ATTN_EINVAL;
+    if (!aligned(q_f16, 16) || !aligned(k_f16, 16) || !aligned(q_f8, 16) || !aligned(k_f8, 16) ||
+        !aligned(workspace, 16) || !aligned(q_scale, 4) || !aligned(k_scale, 4) ||
+        (k_mean && !aligned(k_mean, 4)))
+        return ATTN_EINVAL;
+    size_t mean_off = 0;
+    QuantWorkspace ws;
+    quant_workspace_layout(*shape, &mean_off, &ws.nchunk);
+    ws.partial = static_cast<long long*>(workspace);
+    ws.mean = reinterpret_cast<float*>(static_cast<char*>(workspace) + mean_off);
+    return launch_quantize(*shape, q_f16, k_f16, reinterpret_cast<int8_t*>(q_f8), q_scale,
+                           reinterpret_cast<int8_t*>(k_f8), k_scale, k_mean, ws,
+                           static_cast<hipStream_t>(stream), true);
+}
+
+int attn_fwd_fp8(const attn_shape* shape, const uint8_t* q_f8, const float* q_scale,
+                 const uint8_t* k_f8, const float* k_scale, const void* v_f16, void* o_f16,
+                 float* lse, const int32_t* kv_head_map, int causal, float sm_scale, void* stream) {
+    int st = check_shape(shape);
+    if (st != ATTN_OK) return st;
+    if (!q_f8 || !q_scale || !k_f8 || !k_scale || !v_f16 || !o_f16) return ATTN_EINVAL;
+    if (!aligned(q_f8, 16) || !aligned(k_f8, 16) || !aligned(v_f16, 16) || !aligned(o_f16, 16) ||
+        !aligned(q_scale, 4) || !aligned(k_scale, 4) || (lse && !aligned(lse, 4)))
+        return ATTN_EINVAL;
+    FwdParams p;
+    std::memset(&p, 0, sizeof(p));
+    if ((st = build_map(*shape, kv_head_map, &p)) != ATTN_OK) return st;
+    if ((st = check_scale(sm_scale, shape->head_dim, &p.scale_log2)) != ATTN_OK) return st;
+    fill_common(*shape, &p);
+    p.q = q_f8;
+    p.k = k_f8;
+    p.v = v_f16;
+    p.o = o_f16;
+    p.lse = lse;
+    p.q_scale = q_scale;
+    p.k_scale = k_scale;
+    return launch_fwd(FwdKind::kFp8, shape->head_dim, causal != 0, p, static_cast<hipStream_t>(stream));
+}
+
+int64_t attn_v_fp8_stride(const attn_shape* shape) {
+    if (check_shape(shape) != ATTN_OK) return 0;
+    return static_cast<int64_t>(ceil_div(shape->seq, kBK)) * kBK;
+}
+
+int attn_quantize_v_fp8(const attn_shape* shape, const void* v_f16, uint8_t* v_f8t, float* v_scale,
+                        void* workspace, void* stream) {
+    int st = check_shape(shape);
+    if (st != ATTN_OK) return st;
+    if (!v_f16 || !v_f8t || !v_scale || !workspace) return ATTN_EINVAL;
+    if (!aligned(v_f16, 16) || !aligned(v_f8t, 16) || !aligned(workspace, 16) || !aligned(v_scale, 4))
+        return ATTN_EINVAL;
+    size_t mean_off = 0;
+    QuantWorkspace ws;
+    quant_workspace_layout(*shape, &mean_off, &ws.nchunk);
+    ws.partial = static_cast<long long*>(workspace);
+    ws.mean = reinterpret_cast<float*>(static_cast<char*>(workspace) + mean_off);
+    return launch_quantize_v_fp8(*shape, v_f16, v_f8t, v_scale, ws, static_cast<hipStream_t>(stream));
+}
+
+int attn_fwd_int8_pv8(const attn_shape* shape, const int8_t* q_i8, const float* q_scale,
+                      const int8_t* k_i8, const float* k_scale, const uint8_t* v_f8t,
+                      const float* v_scale, void* o_f16, float* lse, const int32_t* kv_head_map,
+                      int causal, float sm_scale, void* stream) {
+    int st = check_shape(shape);
+    if (st != ATTN_OK) return st;
+    if (!q_i8 || !q_scale || !k_i8 || !k_scale || !v_f8t || !v_scale || !o_f16) return ATTN_EINVAL;
+    if (!aligned(q_i8, 16) || !aligned(k_i8, 16) || !aligned(v_f8t, 16) || !aligned(o_f16, 16) ||
+        !aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(v_scale, 4) || (lse && !aligned(lse, 4)))
+        return ATTN_EINVAL;
+    FwdParams p;
+    std::memset(&p, 0, sizeof(p));
+    if ((st = build_map(*shape, kv_head_map, &p)) != ATTN_OK) return st;
+    if ((st = check_scale(sm_scale, shape->head_dim, &p.scale_log2)) != ATTN_OK) return st;
+    fill_common(*shape, &p);
+    p.q = q_i8;
+    p.k = k_i8;
+    p.v = v_f8t;
+    p.o = o_f16;
+    p.lse = lse;
+    p.q_scale = q_scale;
+    p.k_scale = k_scale;
+    p.v_scale = v_scale;
+    return launch_fwd(FwdKind::kInt8Pv8, shape->head_dim, causal != 0, p, static_cast<hipStream_t>(stream));
+}
+
 const char* attn_status_string(int status) {
     switch (status) {
         case ATTN_OK: return "ok";

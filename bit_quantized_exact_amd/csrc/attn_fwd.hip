@@ -62,25 +62,33 @@ typedef float f2 __attribute__((ext_vector_type(2)));
 typedef float f16x __attribute__((ext_vector_type(16)));
 typedef int i16x __attribute__((ext_vector_type(16)));
 typedef int i4x __attribute__((ext_vector_type(4)));
+typedef int i8x __attribute__((ext_vector_type(8)));
+typedef int i2x __attribute__((ext_vector_type(2)));
 typedef __fp16 tr4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
 typedef __attribute__((address_space(3))) tr4 lds_tr4;
 
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.0f;   // log2 headroom before the running max is raised
 
-template <int D, bool INT8>
+// F8: the 8-bit Q/K codes are E4M3 (FP8 alternative) instead of INT8.
+// PV8: the 8-bit P.V ablation (E4M3 P, E4M3 V stored as V^T tiles).
+template <int D, bool INT8, bool F8 = false, bool PV8 = false>
 struct Cfg : geom::Stage<D, INT8> {
     using G = geom::Stage<D, INT8>;
-    using G::KELT, G::KROWG, G::KCPR, G::VCPR, G::KPT, G::VPT, G::QSTEPS;
+    using G::KELT, G::KROWG, G::KCPR, G::VCPR, G::KPT, G::QSTEPS;
     static constexpr int KROW = KROWG + 16;                    // K row bytes in LDS
-    static constexpr int VROW = 2 * D + 64;                    // V row bytes in LDS
+    // V tile in LDS: 64 key rows of 2D bytes (+ padding), or for PV8 D rows
+    // of 64 key bytes (+ padding) split into the two lane halves' key sets
+    static constexpr int VROW = PV8 ? 64 + 16 : 2 * D + 64;
+    static constexpr int VPT = PV8 ? geom::StageV8<D>::VPT : G::VPT;
     static constexpr int KBYTES = kBN * KROW;
-    static constexpr int VBYTES = kBN * VROW;
+    static constexpr int VBYTES = (PV8 ? D : kBN) * VROW;
     static constexpr int DT = D / 32;                          // 32-row d tiles of O^T
     static_assert(kBN * KCPR % kFwdThreads == 0 && kBN * VCPR % kFwdThreads == 0, "tile split");
     static_assert(geom::kTileM == kBM && geom::kTileN == kBN && geom::kThreads == kFwdThreads, "geometry");
+    static_assert(!F8 || (INT8 && QSTEPS % 2 == 0), "FP8 scores pair two 16-byte k-steps");
     typedef std::conditional_t<INT8, i4x, h8> qfrag_t;         // B operand fragment of Q
-    typedef std::conditional_t<INT8, i16x, f16x> acc_t;        // 32x32 score accumulator
+    typedef std::conditional_t<INT8 && !F8, i16x, f16x> acc_t; // 32x32 score accumulator
 };
 
 __device__ __forceinline__ h8 join(tr4 a, tr4 b) {
@@ -116,12 +124,31 @@ __device__ __forceinline__ float row_sum(float x) {
 // Transposed scores of one 64-key tile for this wave's 32 queries:
 // acc[mt] holds keys mt*32 + (r/4)*8 + (lane/32)*4 + r%4 (register r) of query
 // lane%32.  The same code feeds the forward and the INT32 score dump.
-template <int D, bool INT8>
-__device__ __forceinline__ void score_tile(const char* ks, const typename Cfg<D, INT8>::qfrag_t* qf,
-                                           int l32, int g, typename Cfg<D, INT8>::acc_t acc[2]) {
-    using C = Cfg<D, INT8>;
+// For F8 two consecutive 16-byte k-steps form one 32-byte operand of
+// v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3, fp32 accumulation); A and B take
+// their bytes from the same k positions, so the products pair up as in the
+// INT8 form.
+template <int D, bool INT8, bool F8 = false>
+__device__ __forceinline__ void score_tile(const char* ks, const typename Cfg<D, INT8, F8>::qfrag_t* qf,
+                                           int l32, int g, typename Cfg<D, INT8, F8>::acc_t acc[2]) {
+    using C = Cfg<D, INT8, F8>;
     acc[0] = typename C::acc_t{};
     acc[1] = typename C::acc_t{};
+    if constexpr (F8) {
+#pragma unroll
+        for (int s2 = 0; s2 < C::QSTEPS / 2; ++s2) {
+            const i8x b = __builtin_shufflevector(qf[2 * s2], qf[2 * s2 + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                const char* row = ks + (mt * 32 + l32) * C::KROW + g * 16;
+                const i4x a0 = *reinterpret_cast<const i4x*>(row + (2 * s2) * 32);
+                const i4x a1 = *reinterpret_cast<const i4x*>(row + (2 * s2 + 1) * 32);
+                const i8x a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+                acc[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[mt], 0, 0, 0, 0, 0, 0);
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int s = 0; s < C::QSTEPS; ++s) {
 #pragma unroll
@@ -139,11 +166,13 @@ __device__ __forceinline__ void score_tile(const char* ks, const typename Cfg<D,
 
 using geom::key_offset;
 
-template <int D, bool INT8, bool CAUSAL, bool DUMP, bool QF16 = false>
+template <int D, bool INT8, bool CAUSAL, bool DUMP, bool QF16 = false, bool F8 = false, bool PV8 = false>
 __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(const FwdParams p) {
     static_assert(!QF16 || (INT8 && !DUMP), "in-kernel Q quantisation is an INT8 forward variant");
-    using C = Cfg<D, INT8>;
+    static_assert(!F8 || (INT8 && !DUMP && !QF16 && !PV8), "FP8 scores: standalone-quantised Q/K");
+    static_assert(!PV8 || (INT8 && !DUMP && !QF16 && !F8), "8-bit P.V: INT8 Q/K");
+    using C = Cfg<D, INT8, F8, PV8>;
     typedef typename C::qfrag_t qfrag_t;
     typedef typename C::acc_t acc_t;
     __shared__ __attribute__((aligned(16))) char smem[2 * C::KBYTES + (DUMP ? 0 : 2 * C::VBYTES)];
@@ -178,7 +207,9 @@ void fwd_kernel(const FwdParams p) {
     // Rows past the sequence are read from row S-1 (always in bounds) and
     // masked out of the softmax.
     const char* kg = static_cast<const char*>(p.k) + bhk * S * C::KROWG;
-    const char* vg = static_cast<const char*>(p.v) + bhk * S * C::VROWG;
+    const int vt_stride = p.nkblk * kBN;   // PV8: key columns per V^T row
+    const char* vg = static_cast<const char*>(p.v) +
+                     (PV8 ? bhk * static_cast<size_t>(D) * vt_stride : bhk * S * C::VROWG);
     // Addresses: a wave-uniform tile base plus a 32-bit per-lane offset
     // (row clamped to the sequence), so the loads use the scalar-base form.
     // Register sets for staging (a second set when prefetching two tiles ahead).
@@ -196,6 +227,17 @@ void fwd_kernel(const FwdParams p) {
         }
     };
     auto gload_v = [&](int n0, i4x (&dst)[C::VPT]) {
+        if constexpr (PV8) {
+            const char* base = vg + geom::v8_tile_col(n0, p.nkblk);
+#pragma unroll
+            for (int i = 0; i < C::VPT; ++i) {
+                const int c = tid + kFwdThreads * i;
+                const uint32_t off = static_cast<uint32_t>(c / geom::kV8ChunksPerRow) * vt_stride +
+                                     (c % geom::kV8ChunksPerRow) * 16;
+                dst[i] = *reinterpret_cast<const i4x*>(base + off);
+            }
+            return;
+        }
         const int first = geom::tile_first_row(n0, S);
         const char* base = vg + static_cast<size_t>(first) * C::VROWG;
 #pragma unroll
@@ -216,6 +258,23 @@ void fwd_kernel(const FwdParams p) {
     };
     auto sstore_v = [&](int stage, const i4x (&src)[C::VPT]) {
         char* vs = vbuf(stage);
+        if constexpr (PV8) {
+            // chunk part q16 of row d holds keys 16 q16 .. +15; dwords 0 and 2
+            // (keys +0..3, +8..11) belong to lanes 0-31, dwords 1 and 3 to
+            // lanes 32-63.  Each half is stored in the order its MFMA operand
+            // slots take the keys: slot mt*16 + r <-> key_offset(mt, r) + 4 g.
+#pragma unroll
+            for (int i = 0; i < C::VPT; ++i) {
+                const int c = tid + kFwdThreads * i;
+                const int d = c / geom::kV8ChunksPerRow, q16 = c % geom::kV8ChunksPerRow;
+                char* row = vs + d * C::VROW + (q16 >> 1) * 16 + (q16 & 1) * 8;
+                const i2x lo = {src[i][0], src[i][2]};
+                const i2x hi = {src[i][1], src[i][3]};
+                *reinterpret_cast<i2x*>(row) = lo;
+                *reinterpret_cast<i2x*>(row + 32) = hi;
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < C::VPT; ++i) {
             const int c = tid + kFwdThreads * i;
@@ -331,7 +390,7 @@ void fwd_kernel(const FwdParams p) {
         acc_t sc[2];
         sstore_k(0, kreg[0]);
         __syncthreads();
-        score_tile<D, INT8>(kbuf(0), qf, l32, g, sc);
+        score_tile<D, INT8, F8>(kbuf(0), qf, l32, g, sc);
         gload_k(kBN, kreg[0]);
         gload_v(0, vreg[0]);
         sstore_k(1, kreg[0]);
@@ -377,7 +436,8 @@ void fwd_kernel(const FwdParams p) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, sv[mt][r]);
                 const float m_tile = row_max(mx) * c;
-                if (__ballot(m_tile > m_run + kLazy)) {
+                // (8-bit P needs p <= 1: no lazy headroom there)
+                if (__ballot(m_tile > m_run + (PV8 ? 0.0f : kLazy))) {
                     const float m_new = fmaxf(m_run, m_tile);
                     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
                     m_run = m_new;
@@ -388,7 +448,7 @@ void fwd_kernel(const FwdParams p) {
 
                 // scores of the next tile (MFMA) overlap the exponentials (VALU)
                 acc_t sn[2];
-                score_tile<D, INT8>(kbuf((j + 1) & 1), qf, l32, g, sn);
+                score_tile<D, INT8, F8>(kbuf((j + 1) & 1), qf, l32, g, sn);
 
                 const float negm = -m_run;
                 float pv[2][16];
@@ -403,6 +463,29 @@ void fwd_kernel(const FwdParams p) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) psum += pv[mt][r];
                 l_run += psum;
+                if constexpr (PV8) {
+                    // ---- O^T += V8^T P8^T: E4M3(448 p) in operand slot
+                    // mt*16 + r, V codes from the split rows (one MFMA per d tile)
+                    i8x pb8;
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        const float* q = &pv[k >> 2][(k & 3) * 4];
+                        int w = __builtin_amdgcn_cvt_pk_fp8_f32(q[0] * 448.0f, q[1] * 448.0f, 0, false);
+                        w = __builtin_amdgcn_cvt_pk_fp8_f32(q[2] * 448.0f, q[3] * 448.0f, w, true);
+                        pb8[k] = w;
+                    }
+                    const char* vs = vbuf(j & 1);
+#pragma unroll
+                    for (int dt = 0; dt < C::DT; ++dt) {
+                        const char* row = vs + (dt * 32 + l32) * C::VROW + g * 32;
+                        const i4x a0 = *reinterpret_cast<const i4x*>(row);
+                        const i4x a1 = *reinterpret_cast<const i4x*>(row + 16);
+                        const i8x a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+                        oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb8, oacc[dt], 0, 0, 0, 0, 0, 0);
+                    }
+                    sc[0] = sn[0];
+                    sc[1] = sn[1];
+                } else {
                 h8 pb[4];
 #pragma unroll
                 for (int k4 = 0; k4 < 4; ++k4) {
@@ -434,6 +517,7 @@ void fwd_kernel(const FwdParams p) {
                 }
                 sc[0] = sn[0];
                 sc[1] = sn[1];
+                }
             }
             sstore_k(j & 1, kreg[SS]);
             sstore_v((j + 1) & 1, vreg[SS]);
@@ -457,6 +541,18 @@ void fwd_kernel(const FwdParams p) {
         const float inv = 1.0f / l_tot;
         if (qi < S) {
             _Float16* orow = static_cast<_Float16*>(p.o) + (bhq * S + static_cast<size_t>(qi)) * D;
+            if constexpr (PV8) {
+                // undo the 448 of P8 and apply the per-channel V scales
+                const float* vsc = p.v_scale + bhk * D;
+#pragma unroll
+                for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+                    for (int j4 = 0; j4 < 4; ++j4) {
+                        const int col = geom::o_column(dt, j4, g);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) oacc[dt][j4 * 4 + e] *= vsc[col + e] * (1.0f / 448.0f);
+                    }
+            }
 #pragma unroll
             for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
@@ -470,10 +566,10 @@ void fwd_kernel(const FwdParams p) {
     }
 }
 
-template <int D, bool INT8, bool CAUSAL, bool DUMP, bool QF16 = false>
+template <int D, bool INT8, bool CAUSAL, bool DUMP, bool QF16 = false, bool F8 = false, bool PV8 = false>
 void launch_one(const FwdParams& p, hipStream_t st) {
     const int blocks = p.B * p.Hq * p.ntiles;
-    hipLaunchKernelGGL((fwd_kernel<D, INT8, CAUSAL, DUMP, QF16>), dim3(blocks), dim3(kFwdThreads), 0, st, p);
+    hipLaunchKernelGGL((fwd_kernel<D, INT8, CAUSAL, DUMP, QF16, F8, PV8>), dim3(blocks), dim3(kFwdThreads), 0, st, p);
 }
 
 template <int D>
@@ -490,6 +586,14 @@ void launch_d(FwdKind kind, bool causal, const FwdParams& p, hipStream_t st) {
             break;
         case FwdKind::kInt8FusedQ:
             causal ? launch_one<D, true, true, false, true>(p, st) : launch_one<D, true, false, false, true>(p, st);
+            break;
+        case FwdKind::kFp8:
+            causal ? launch_one<D, true, true, false, false, true>(p, st)
+                   : launch_one<D, true, false, false, false, true>(p, st);
+            break;
+        case FwdKind::kInt8Pv8:
+            causal ? launch_one<D, true, true, false, false, false, true>(p, st)
+                   : launch_one<D, true, false, false, false, false, true>(p, st);
             break;
     }
 }

@@ -35,10 +35,16 @@ struct QuantWorkspace {
 // Offsets of the workspace pieces for a shape (256-byte aligned pieces).
 size_t quant_workspace_layout(const attn_shape& s, size_t* mean_offset, int* nchunk);
 
-// q may be null (K only): then q_i8 and q_scale are not touched.
+// q may be null (K only): then q_i8 and q_scale are not touched.  fp8
+// selects E4M3 codes (stored in the int8 buffers) instead of INT8.
 int launch_quantize(const attn_shape& s, const void* q, const void* k, int8_t* q_i8,
                     float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
-                    const QuantWorkspace& ws, hipStream_t st);
+                    const QuantWorkspace& ws, hipStream_t st, bool fp8 = false);
+
+// Per-channel E4M3 V, transposed into [B*Hkv, D, 64*ceil(S/64)] codes, and
+// its scales [B*Hkv, D]; uses the partial-sum area of the workspace.
+int launch_quantize_v_fp8(const attn_shape& s, const void* v, uint8_t* vt, float* v_scale,
+                          const QuantWorkspace& ws, hipStream_t st);
 
 struct FwdParams {
     const void* q;        // fp16 or int8 [B,Hq,S,D]
@@ -50,6 +56,7 @@ struct FwdParams {
     const float* k_scale; // int8 path: [B,Hkv,nkblk]
     int32_t* s_out;       // score dump: [B,Hq,ntiles*BM,S]
     float* q_scale_out;   // fused-Q INT8 path: the Q block scales, [B,Hq,nqblk], or null
+    const float* v_scale; // 8-bit P.V path: per-channel V scales [B,Hkv,D]
     int B, Hq, Hkv, S;
     int nqt;              // query tiles in the sequence
     int nqblk, nkblk;     // scale blocks per (b, head)
@@ -59,7 +66,9 @@ struct FwdParams {
     uint8_t horder[ATTN_MAX_HEADS];  // q-heads ordered by kv-head (launch order)
 };
 
-enum class FwdKind { kFp16, kInt8, kDumpInt8, kInt8FusedQ };
+// kFp8: E4M3 Q/K codes (v_mfma_f32_32x32x64_f8f6f4), FP16 P.V.
+// kInt8Pv8: INT8 Q/K, E4M3 P and per-channel E4M3 V (transposed tiles).
+enum class FwdKind { kFp16, kInt8, kDumpInt8, kInt8FusedQ, kFp8, kInt8Pv8 };
 
 int launch_fwd(FwdKind kind, int head_dim, bool causal, const FwdParams& p, hipStream_t st);
 

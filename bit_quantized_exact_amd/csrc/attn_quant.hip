@@ -113,14 +113,25 @@ __device__ __forceinline__ int quant_one(float x, float r) {
     return static_cast<int>(t);
 }
 
-// One block of ROWS rows of one (b, head) matrix: absmax, scale, int8.
-// SMOOTH subtracts the channel mean first (K); Q is quantised as is.
-template <int D, int ROWS, bool SMOOTH>
+// E4M3 codes of x0*r, x1*r (saturated to +-448 first) in bytes 0 and 1 of
+// the result, v_cvt_pk_fp8_f32 rounding to nearest even.
+__device__ __forceinline__ unsigned e4m3_pair(float x0, float x1, float r) {
+    const float t0 = fminf(fmaxf(x0 * r, -448.0f), 448.0f);
+    const float t1 = fminf(fmaxf(x1 * r, -448.0f), 448.0f);
+    return static_cast<unsigned>(__builtin_amdgcn_cvt_pk_fp8_f32(t0, t1, 0, false)) & 0xffffu;
+}
+
+// One block of ROWS rows of one (b, head) matrix: absmax, scale, 8-bit codes.
+// SMOOTH subtracts the channel mean first (K); Q is quantised as is.  FP8
+// selects the E4M3 grid (448 in place of 127, E4M3 rounding in place of
+// rint + clamp): the FP8 alternative the SageAttention article compares with.
+template <int D, int ROWS, bool SMOOTH, bool FP8 = false>
 __global__ __launch_bounds__(256) void quant_block_kernel(const uint16_t* __restrict__ x,
                                                           const float* __restrict__ mean,
                                                           int8_t* __restrict__ q,
                                                           float* __restrict__ scale, int H,
                                                           int S, int nblk) {
+    constexpr float kTop = FP8 ? 448.0f : 127.0f;
     constexpr int CPR = D / 8;
     constexpr int CHUNKS = ROWS * CPR;
     constexpr int PER = CHUNKS / 256;
@@ -165,16 +176,21 @@ __global__ __launch_bounds__(256) void quant_block_kernel(const uint16_t* __rest
         for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[i][e]));
     }
     const float a = block_max(amax, red);
-    const float r = (a == 0.0f) ? 0.0f : __fdiv_rn(127.0f, a);
+    const float r = (a == 0.0f) ? 0.0f : __fdiv_rn(kTop, a);
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int row = r0 + (t + 256 * i) / CPR;
         if (row < S) {
             unsigned packed[2] = {0u, 0u};
+            if constexpr (FP8) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const unsigned b8 = static_cast<unsigned>(quant_one(v[i][e], r)) & 0xffu;
-                packed[e / 4] |= b8 << (8 * (e % 4));
+                for (int e = 0; e < 8; e += 2) packed[e / 4] |= e4m3_pair(v[i][e], v[i][e + 1], r) << (8 * (e % 4));
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const unsigned b8 = static_cast<unsigned>(quant_one(v[i][e], r)) & 0xffu;
+                    packed[e / 4] |= b8 << (8 * (e % 4));
+                }
             }
             i2x out;
             out[0] = static_cast<int>(packed[0]);
@@ -182,10 +198,100 @@ __global__ __launch_bounds__(256) void quant_block_kernel(const uint16_t* __rest
             *reinterpret_cast<i2x*>(qb + static_cast<size_t>(row) * D + cc * 8) = out;
         }
     }
-    if (t == 0) scale[mat * nblk + blk] = (a == 0.0f) ? 0.0f : __fdiv_rn(a, 127.0f);
+    if (t == 0) scale[mat * nblk + blk] = (a == 0.0f) ? 0.0f : __fdiv_rn(a, kTop);
 }
 
+// 8-bit V of the P.V ablation, pass 1: per (b, kv-head, chunk of kSumChunk
+// tokens) the column maxima of |V| (exact, any order).
 template <int D>
+__global__ __launch_bounds__(256) void v_colmax_kernel(const uint16_t* __restrict__ v, int S,
+                                                       int nchunk, float* __restrict__ partial) {
+    constexpr int CPR = D / 8;
+    constexpr int RG = 256 / CPR;
+    __shared__ float red[RG][D];
+    const int t = threadIdx.x;
+    const int cc = t % CPR, rg = t / CPR;
+    const int chunk = blockIdx.x;
+    const size_t bk = blockIdx.y;
+    const uint16_t* base = v + bk * static_cast<size_t>(S) * D;
+    float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    const int r0 = chunk * kSumChunk;
+    for (int r = r0 + rg; r < r0 + kSumChunk && r < S; r += RG) {
+        const i4x w = *reinterpret_cast<const i4x*>(base + static_cast<size_t>(r) * D + cc * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const unsigned u = static_cast<unsigned>(w[e]);
+            m[2 * e] = fmaxf(m[2 * e], fabsf(half_bits_to_float(u & 0xffffu)));
+            m[2 * e + 1] = fmaxf(m[2 * e + 1], fabsf(half_bits_to_float(u >> 16)));
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[rg][cc * 8 + e] = m[e];
+    __syncthreads();
+    if (t < D) {
+        float a = 0.0f;
+        for (int g = 0; g < RG; ++g) a = fmaxf(a, red[g][t]);
+        partial[(bk * nchunk + chunk) * D + t] = a;
+    }
+}
+
+// Pass 2, per (b, kv-head, 64-key tile): a_c = max over the chunks,
+// r_c = 448/a_c, code = E4M3(clamp(v r_c)), written TRANSPOSED: vt is
+// [B*Hkv, D, Sp] with Sp = 64 * ceil(S/64) and zero codes for keys >= S.
+// Tile 0 also writes delta_c = a_c/448.
+template <int D>
+__global__ __launch_bounds__(256) void v_quant_kernel(const uint16_t* __restrict__ v, int S,
+                                                      int nchunk, const float* __restrict__ partial,
+                                                      uint8_t* __restrict__ vt,
+                                                      float* __restrict__ v_scale) {
+    constexpr int CPR = D / 8;                 // 16-byte chunks per V row
+    constexpr int IN_PER = 64 * CPR / 256;     // input chunks per thread
+    constexpr int OUT_PER = D * 4 / 256;       // 16-byte output chunks per thread
+    constexpr int TROW = 64 + 16;              // transposed tile row bytes in LDS
+    __shared__ float rs[D];
+    __shared__ __attribute__((aligned(16))) uint8_t tile[D * TROW];
+    const int t = threadIdx.x;
+    const int n0 = blockIdx.x * 64;
+    const size_t bk = blockIdx.y;
+    const int Sp = gridDim.x * 64;
+    if (t < D) {
+        float a = 0.0f;
+        for (int i = 0; i < nchunk; ++i) a = fmaxf(a, partial[(bk * nchunk + i) * D + t]);
+        rs[t] = a == 0.0f ? 0.0f : __fdiv_rn(448.0f, a);
+        if (blockIdx.x == 0) v_scale[bk * D + t] = a == 0.0f ? 0.0f : __fdiv_rn(a, 448.0f);
+    }
+    __syncthreads();
+    const uint16_t* base = v + bk * static_cast<size_t>(S) * D;
+#pragma unroll
+    for (int i = 0; i < IN_PER; ++i) {
+        const int c = t + 256 * i;
+        const int row = c / CPR, cc = c % CPR;
+        i4x w = {0, 0, 0, 0};
+        if (n0 + row < S) w = *reinterpret_cast<const i4x*>(base + static_cast<size_t>(n0 + row) * D + cc * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const unsigned u = static_cast<unsigned>(w[e]);
+            const int ch = cc * 8 + 2 * e;
+            const float x0 = half_bits_to_float(u & 0xffffu), x1 = half_bits_to_float(u >> 16);
+            // (each value converted as both halves of a pair: the byte is then the same in either slot)
+            const unsigned lo = e4m3_pair(x0, x0, rs[ch]) & 0xffu;
+            const unsigned hi = e4m3_pair(x1, x1, rs[ch + 1]) & 0xffu;
+            tile[ch * TROW + row] = static_cast<uint8_t>(lo);
+            tile[(ch + 1) * TROW + row] = static_cast<uint8_t>(hi);
+        }
+    }
+    __syncthreads();
+    uint8_t* out = vt + bk * static_cast<size_t>(D) * Sp + n0;
+#pragma unroll
+    for (int i = 0; i < OUT_PER; ++i) {
+        const int c = t + 256 * i;
+        const int d = c / 4, part = c % 4;
+        *reinterpret_cast<i4x*>(out + static_cast<size_t>(d) * Sp + part * 16) =
+            *reinterpret_cast<const i4x*>(tile + d * TROW + part * 16);
+    }
+}
+
+template <int D, bool FP8>
 int launch_quantize_d(const attn_shape& s, const void* q, const void* k, int8_t* q_i8,
                       float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
                       const QuantWorkspace& ws, hipStream_t st) {
@@ -198,10 +304,10 @@ int launch_quantize_d(const attn_shape& s, const void* q, const void* k, int8_t*
     hipLaunchKernelGGL(k_mean_kernel<D>, dim3(BH_kv), dim3(D), 0, st, ws.partial, S, ws.nchunk,
                        ws.mean, k_mean);
     const int nkb = ceil_div(S, kBK), nqb = ceil_div(S, kBQ);
-    hipLaunchKernelGGL((quant_block_kernel<D, kBK, true>), dim3(nkb, s.heads_kv, s.batch),
+    hipLaunchKernelGGL((quant_block_kernel<D, kBK, true, FP8>), dim3(nkb, s.heads_kv, s.batch),
                        dim3(256), 0, st, kk, ws.mean, k_i8, k_scale, s.heads_kv, S, nkb);
     if (qq)
-        hipLaunchKernelGGL((quant_block_kernel<D, kBQ, false>), dim3(nqb, s.heads_q, s.batch),
+        hipLaunchKernelGGL((quant_block_kernel<D, kBQ, false, FP8>), dim3(nqb, s.heads_q, s.batch),
                            dim3(256), 0, st, qq, static_cast<const float*>(nullptr), q_i8, q_scale,
                            s.heads_q, S, nqb);
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ELAUNCH;
@@ -222,10 +328,30 @@ size_t quant_workspace_layout(const attn_shape& s, size_t* mean_offset, int* nch
 
 int launch_quantize(const attn_shape& s, const void* q, const void* k, int8_t* q_i8,
                     float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
-                    const QuantWorkspace& ws, hipStream_t st) {
+                    const QuantWorkspace& ws, hipStream_t st, bool fp8) {
     if (s.head_dim == 64)
-        return launch_quantize_d<64>(s, q, k, q_i8, q_scale, k_i8, k_scale, k_mean, ws, st);
-    return launch_quantize_d<128>(s, q, k, q_i8, q_scale, k_i8, k_scale, k_mean, ws, st);
+        return fp8 ? launch_quantize_d<64, true>(s, q, k, q_i8, q_scale, k_i8, k_scale, k_mean, ws, st)
+                   : launch_quantize_d<64, false>(s, q, k, q_i8, q_scale, k_i8, k_scale, k_mean, ws, st);
+    return fp8 ? launch_quantize_d<128, true>(s, q, k, q_i8, q_scale, k_i8, k_scale, k_mean, ws, st)
+               : launch_quantize_d<128, false>(s, q, k, q_i8, q_scale, k_i8, k_scale, k_mean, ws, st);
+}
+
+int launch_quantize_v_fp8(const attn_shape& s, const void* v, uint8_t* vt, float* v_scale,
+                          const QuantWorkspace& ws, hipStream_t st) {
+    const int S = s.seq;
+    const int BH_kv = s.batch * s.heads_kv;
+    const uint16_t* vv = static_cast<const uint16_t*>(v);
+    // the column maxima reuse the partial-sum area of the workspace (4 of its 8 bytes per entry)
+    float* part = reinterpret_cast<float*>(ws.partial);
+    const int ntile = ceil_div(S, 64);
+    if (s.head_dim == 64) {
+        hipLaunchKernelGGL(v_colmax_kernel<64>, dim3(ws.nchunk, BH_kv), dim3(256), 0, st, vv, S, ws.nchunk, part);
+        hipLaunchKernelGGL(v_quant_kernel<64>, dim3(ntile, BH_kv), dim3(256), 0, st, vv, S, ws.nchunk, part, vt, v_scale);
+    } else {
+        hipLaunchKernelGGL(v_colmax_kernel<128>, dim3(ws.nchunk, BH_kv), dim3(256), 0, st, vv, S, ws.nchunk, part);
+        hipLaunchKernelGGL(v_quant_kernel<128>, dim3(ntile, BH_kv), dim3(256), 0, st, vv, S, ws.nchunk, part, vt, v_scale);
+    }
+    return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ELAUNCH;
 }
 
 }  // namespace attn

@@ -89,6 +89,19 @@ struct Stage {
     }
 };
 
+// 8-bit V of the P.V ablation: V^T codes [B*Hkv, D, Sp], Sp = 64 * nkblk.
+// A key tile at n0 is D rows of 64 bytes starting at column
+// v8_tile_col(n0, nkblk); tiles prefetched past the end are clamped to the
+// last tile (always inside the buffer).  Thread chunk c (16 bytes) covers row
+// d = c / 4, bytes (c % 4) * 16 of the tile.
+constexpr int kV8ChunksPerRow = 4;
+__host__ __device__ inline int v8_tile_col(int n0, int nkblk) { return imin(n0, (nkblk - 1) * kTileN); }
+template <int D>
+struct StageV8 {
+    static constexpr int VPT = D * kV8ChunksPerRow / kThreads;   // 16-byte chunks per thread
+    static_assert(D * kV8ChunksPerRow % kThreads == 0, "tile split");
+};
+
 // Score register r of 32-key sub-tile mt (32x32 MFMA accumulator layout)
 // holds key n0 + g*4 + key_offset(mt, r) of a tile at n0 (g = lane / 32).
 __host__ __device__ constexpr int key_offset(int mt, int r) { return mt * 32 + (r >> 2) * 8 + (r & 3); }

@@ -167,6 +167,59 @@ int attn_debug_qk_int32(const attn_shape* shape, const int8_t* q_i8, const int8_
                         const int32_t* kv_head_map, int causal, int32_t q_tile_lo,
                         int32_t q_tile_hi, int32_t* s_out, void* stream);
 
+/* ---- FP8 alternative and 8-bit P.V ablation ------------------------------
+ * [SA] 技术方案 chooses INT8 for Q and K because it is more accurate than FP8,
+ * and keeps P and V in FP16 because 8-bit P and V (INT8, E4M3 or E5M2) lose
+ * accuracy in some layers.  These calls provide both alternatives on the
+ * gfx950 FP8 matrix cores so the claims can be measured.  FP8 means OCP E4M3
+ * (bias 7, largest magnitude 448, no infinities); codes are stored one byte per
+ * element and converted with round-to-nearest-even. */
+
+/* As attn_quantize_qk (same mean, smoothing, blocks and workspace), but with
+ * the E4M3 grid: per block a = max|x|; a == 0 gives r = 0 (codes of +-0) and
+ * delta = 0; otherwise r = 448/a and delta = a/448 (fp32, correctly rounded)
+ * and the code is E4M3(clamp(x*r, -448, 448)), x*r one fp32 product, the sign
+ * of a zero product kept.  q_f8 [B,Hq,S,D], k_f8 [B,Hkv,S,D] E4M3 codes. */
+int attn_quantize_qk_fp8(const attn_shape* shape, const void* q_f16, const void* k_f16,
+                         uint8_t* q_f8, float* q_scale, uint8_t* k_f8, float* k_scale,
+                         float* k_mean, void* workspace, void* stream);
+
+/* Attention forward with E4M3 Q/K: as attn_fwd_int8, with
+ *   s[i,j] = (sum_c dec(q_f8[i,c]) dec(k_f8[j,c])) * q_scale * k_scale * sm_scale,
+ * the sum on the FP8 matrix cores with fp32 accumulation (products are exact;
+ * the accumulation order is the hardware's).  P and V as attn_fwd_int8. */
+int attn_fwd_fp8(const attn_shape* shape, const uint8_t* q_f8, const float* q_scale,
+                 const uint8_t* k_f8, const float* k_scale, const void* v_f16, void* o_f16,
+                 float* lse, const int32_t* kv_head_map, int causal, float sm_scale, void* stream);
+
+/* Row stride, in bytes (= keys), of the transposed 8-bit V that
+ * attn_quantize_v_fp8 writes: 64 * ceil(seq / 64).  0 for an invalid shape. */
+int64_t attn_v_fp8_stride(const attn_shape* shape);
+
+/* 8-bit V for the P.V ablation: one E4M3 scale per (b, kv-head, channel) over
+ * all tokens: a_c = max_j |V[b,k,j,c]|, r = 448/a_c, delta_c = a_c/448 (fp32,
+ * correctly rounded; a_c == 0 gives r = 0, delta_c = 0), code =
+ * E4M3(clamp(v*r, -448, 448)).  The codes are written TRANSPOSED, the layout
+ * the P.V matrix-core operand wants:
+ *   v_f8t [B, Hkv, D, stride] with v_f8t[b,k,c,j] = code of V[b,k,j,c] for
+ *   j < seq and 0 for seq <= j < stride (stride = attn_v_fp8_stride).
+ * v_scale out fp32 [B,Hkv,D].  workspace: attn_quantize_workspace_bytes(shape)
+ * bytes, 16-byte aligned, contents ignored. */
+int attn_quantize_v_fp8(const attn_shape* shape, const void* v_f16, uint8_t* v_f8t,
+                        float* v_scale, void* workspace, void* stream);
+
+/* Attention forward with INT8 Q/K (as attn_fwd_int8) and 8-bit P and V: the
+ * online softmax (running maximum raised whenever a key tile exceeds it, so
+ * every weight p <= 1) rounds each weight to E4M3(448 p) against the running
+ * maximum of its 64-key tile; P.V runs on the FP8 matrix cores with fp32
+ * accumulation; the row sum uses the unrounded weights;
+ *   O[i,c] = delta_c / 448 * (sum_j E4M3(448 p_ij) dec(v_f8t[c,j])) / rowsum.
+ * v_f8t, v_scale from attn_quantize_v_fp8.  Other arguments as attn_fwd_int8. */
+int attn_fwd_int8_pv8(const attn_shape* shape, const int8_t* q_i8, const float* q_scale,
+                      const int8_t* k_i8, const float* k_scale, const uint8_t* v_f8t,
+                      const float* v_scale, void* o_f16, float* lse, const int32_t* kv_head_map,
+                      int causal, float sm_scale, void* stream);
+
 /* Static text for a status code. */
 const char* attn_status_string(int status);
 

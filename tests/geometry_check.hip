@@ -28,9 +28,11 @@ static long g_errors = 0;
         }                                                                 \
     } while (0)
 
+// pv8: the 8-bit P.V variant, whose V tiles come from V^T codes
+// [D, 64 * nkblk] per (b, kv-head) instead of row-major fp16 V.
 template <int D, bool INT8>
 static void check_shape(int B, int Hq, int S, bool causal, bool dump, int tile_lo, int ntiles,
-                        bool all_heads) {
+                        bool all_heads, bool pv8 = false) {
     using St = Stage<D, INT8>;
     const int nqt = (S + kTileM - 1) / kTileM;
     if (!dump) {
@@ -126,6 +128,26 @@ static void check_shape(int B, int Hq, int S, bool causal, bool dump, int tile_l
                     REQUIRE(off + 16 <= qk_head_bytes, "k byte %zu of %zu", off, qk_head_bytes);
                 }
         }
+        if (pv8) {
+            const int Sp = nkblk * kTileN;
+            const size_t vt_head_bytes = static_cast<size_t>(D) * Sp;
+            for (int n0 : vn0) {
+                const int col = v8_tile_col(n0, nkblk);
+                REQUIRE(col >= 0 && col % kTileN == 0 && col + kTileN <= Sp, "v8 column %d (n0 %d, Sp %d)", col, n0, Sp);
+                for (int tid = 0; tid < kThreads; ++tid)
+                    for (int i = 0; i < StageV8<D>::VPT; ++i) {
+                        const int cidx = tid + kThreads * i;
+                        const int d = cidx / kV8ChunksPerRow, part = cidx % kV8ChunksPerRow;
+                        REQUIRE(d >= 0 && d < D, "v8 row %d", d);
+                        const long long off32 = static_cast<long long>(d) * Sp + part * 16;
+                        REQUIRE(off32 < (1LL << 32), "v8 lane offset %lld", off32);
+                        const size_t off = static_cast<size_t>(col) + static_cast<size_t>(off32);
+                        REQUIRE(off + 16 <= vt_head_bytes, "v8 byte %zu of %zu", off, vt_head_bytes);
+                        REQUIRE(part * 16 + 16 <= kTileN, "v8 chunk %d", part);
+                    }
+            }
+            vn0.clear();
+        }
         for (int n0 : vn0) {
             const int first = tile_first_row(n0, S);
             REQUIRE(first >= 0 && first <= S - 1, "v first row %d", first);
@@ -150,6 +172,7 @@ static void check_all_paths(int B, int Hq, int S, bool all_heads) {
     for (int causal = 0; causal < 2; ++causal) {
         check_shape<D, false>(B, Hq, S, causal, false, 0, 0, all_heads);
         check_shape<D, true>(B, Hq, S, causal, false, 0, 0, all_heads);
+        check_shape<D, true>(B, Hq, S, causal, false, 0, 0, all_heads, true);
         check_shape<D, true>(B, Hq, S, causal, true, 0, nqt, all_heads);
         check_shape<D, true>(B, Hq, S, causal, true, nqt - 1, 1, all_heads);
         check_shape<D, true>(B, Hq, S, causal, true, nqt / 2, (nqt + 1) / 2 - nqt / 2 + 1 > 0 ? 1 : 1, all_heads);

@@ -193,3 +193,59 @@ def test_fused_q_validation():
     assert call(shape=_sh(Hq=6, Hkv=4)) == -1
     bad = (ctypes.c_int32 * 4)(0, 1, 2, 0)
     assert call(mp=ctypes.cast(bad, ctypes.c_void_p)) == -4
+
+
+def test_fp8_entry_points_validation():
+    L = A.lib()
+    sh = _sh()
+    P = ctypes.byref(sh)
+    # attn_quantize_qk_fp8: same contract as attn_quantize_qk
+    assert L.attn_quantize_qk_fp8(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == -1
+    for i in range(7):
+        args = [FAKE] * 7
+        args[i] = None
+        q, k, qf, qs, kf, ks, ws = args
+        assert L.attn_quantize_qk_fp8(P, q, k, qf, qs, kf, ks, None, ws, None) == -1
+    assert L.attn_quantize_qk_fp8(P, FAKE, FAKE, MISALIGNED, FAKE, FAKE, FAKE, None, FAKE, None) == -1
+    bad = _sh(D=96)
+    assert L.attn_quantize_qk_fp8(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                  None) == -2
+
+    # attn_fwd_fp8: as attn_fwd_int8
+    def fp8(q=FAKE, qs=FAKE, k=FAKE, ks=FAKE, v=FAKE, o=FAKE, lse=None, mp=None, scale=0.0, shape=sh):
+        return L.attn_fwd_fp8(ctypes.byref(shape) if shape is not None else None, q, qs, k, ks, v, o,
+                              lse, mp, 0, scale, None)
+    assert fp8(shape=None) == -1
+    for arg in ("q", "qs", "k", "ks", "v", "o"):
+        assert fp8(**{arg: None}) == -1
+    assert fp8(k=MISALIGNED) == -1 and fp8(ks=FAKE + 2) == -1 and fp8(lse=FAKE + 2) == -1
+    assert fp8(scale=float("nan")) == -1
+    assert fp8(shape=_sh(Hq=6, Hkv=4)) == -1
+    badmap = (ctypes.c_int32 * 4)(0, 1, 2, 0)
+    assert fp8(mp=ctypes.cast(badmap, ctypes.c_void_p)) == -4
+
+    # the transposed-V stride and its quantiser
+    assert L.attn_v_fp8_stride(ctypes.byref(_sh(S=1))) == 64
+    assert L.attn_v_fp8_stride(ctypes.byref(_sh(S=64))) == 64
+    assert L.attn_v_fp8_stride(ctypes.byref(_sh(S=65))) == 128
+    assert L.attn_v_fp8_stride(ctypes.byref(_sh(D=96))) == 0
+    assert L.attn_v_fp8_stride(None) == 0
+    assert L.attn_quantize_v_fp8(None, FAKE, FAKE, FAKE, FAKE, None) == -1
+    for args in [(None, FAKE, FAKE, FAKE), (FAKE, None, FAKE, FAKE), (FAKE, FAKE, None, FAKE),
+                 (FAKE, FAKE, FAKE, None), (MISALIGNED, FAKE, FAKE, FAKE),
+                 (FAKE, MISALIGNED, FAKE, FAKE), (FAKE, FAKE, FAKE + 2, FAKE)]:
+        assert L.attn_quantize_v_fp8(P, *args, None) == -1
+    assert L.attn_quantize_v_fp8(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, None) == -2
+
+    # attn_fwd_int8_pv8
+    def pv8(q=FAKE, qs=FAKE, k=FAKE, ks=FAKE, vt=FAKE, vs=FAKE, o=FAKE, lse=None, mp=None,
+            scale=0.0, shape=sh):
+        return L.attn_fwd_int8_pv8(ctypes.byref(shape) if shape is not None else None, q, qs, k, ks,
+                                   vt, vs, o, lse, mp, 1, scale, None)
+    assert pv8(shape=None) == -1
+    for arg in ("q", "qs", "k", "ks", "vt", "vs", "o"):
+        assert pv8(**{arg: None}) == -1
+    assert pv8(vt=MISALIGNED) == -1 and pv8(vs=FAKE + 2) == -1
+    assert pv8(scale=float("inf")) == -1
+    assert pv8(shape=bad) == -2
+    assert pv8(mp=ctypes.cast(badmap, ctypes.c_void_p)) == -4
