@@ -68,6 +68,13 @@ typedef __fp16 tr4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
 typedef __attribute__((address_space(3))) tr4 lds_tr4;
 
 constexpr float kLn2 = 0.6931471805599453f;
+// INT8 scores start their INT32 accumulation at the bit pattern of the fp32
+// value 1.5 * 2^23.  While |S32| < 2^22 (it is at most D * 127^2 = 2064512)
+// the accumulator bits then read as the fp32 number 1.5 * 2^23 + S32
+// exactly, so no integer-to-float conversion is needed; the bias is removed
+// inside the fma that scales the score.
+constexpr int kI8BiasBits = 0x4B400000;
+constexpr float kI8Bias = 12582912.0f;
 constexpr float kLazy = 8.0f;   // log2 headroom before the running max is raised
 
 // F8: the 8-bit Q/K codes are E4M3 (FP8 alternative) instead of INT8.
@@ -128,12 +135,18 @@ __device__ __forceinline__ float row_sum(float x) {
 // v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3, fp32 accumulation); A and B take
 // their bytes from the same k positions, so the products pair up as in the
 // INT8 form.
-template <int D, bool INT8, bool F8 = false>
+template <int D, bool INT8, bool F8 = false, bool BIASED = false>
 __device__ __forceinline__ void score_tile(const char* ks, const typename Cfg<D, INT8, F8>::qfrag_t* qf,
                                            int l32, int g, typename Cfg<D, INT8, F8>::acc_t acc[2]) {
     using C = Cfg<D, INT8, F8>;
-    acc[0] = typename C::acc_t{};
-    acc[1] = typename C::acc_t{};
+    static_assert(!BIASED || (INT8 && !F8), "the bias applies to INT32 accumulators");
+    if constexpr (BIASED) {
+        acc[0] = kI8BiasBits;
+        acc[1] = kI8BiasBits;
+    } else {
+        acc[0] = typename C::acc_t{};
+        acc[1] = typename C::acc_t{};
+    }
     if constexpr (F8) {
 #pragma unroll
         for (int s2 = 0; s2 < C::QSTEPS / 2; ++s2) {
@@ -387,10 +400,11 @@ void fwd_kernel(const FwdParams p) {
 
         // ---- prologue: K_0 -> LDS, S_0, then K_1 and V_0 -> LDS (and, at
         // depth 2, K_2 and V_1 into the second register set) ----
+        constexpr bool kBiased = INT8 && !F8;   // INT32 scores read as biased fp32
         acc_t sc[2];
         sstore_k(0, kreg[0]);
         __syncthreads();
-        score_tile<D, INT8, F8>(kbuf(0), qf, l32, g, sc);
+        score_tile<D, INT8, F8, kBiased>(kbuf(0), qf, l32, g, sc);
         gload_k(kBN, kreg[0]);
         gload_v(0, vreg[0]);
         sstore_k(1, kreg[0]);
@@ -421,7 +435,12 @@ void fwd_kernel(const FwdParams p) {
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) sv[mt][r] = static_cast<float>(sc[mt][r]);
+                    for (int r = 0; r < 16; ++r) {
+                        // (through a scalar: __builtin_bit_cast of a vector element
+                        // reads the vector's first element)
+                        if constexpr (kBiased) sv[mt][r] = __int_as_float(static_cast<int>(sc[mt][r]));
+                        else sv[mt][r] = static_cast<float>(sc[mt][r]);
+                    }
                 if (tile_needs_mask(n0)) {
                     const int lim = mask_limit(n0);
 #pragma unroll
@@ -435,7 +454,8 @@ void fwd_kernel(const FwdParams p) {
                 for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, sv[mt][r]);
-                const float m_tile = row_max(mx) * c;
+                // (the biased maximum minus the bias is exact: both lie in [2^23, 2^24))
+                const float m_tile = (kBiased ? row_max(mx) - kI8Bias : row_max(mx)) * c;
                 // (8-bit P needs p <= 1: no lazy headroom there)
                 if (__ballot(m_tile > m_run + (PV8 ? 0.0f : kLazy))) {
                     const float m_new = fmaxf(m_run, m_tile);
@@ -448,9 +468,9 @@ void fwd_kernel(const FwdParams p) {
 
                 // scores of the next tile (MFMA) overlap the exponentials (VALU)
                 acc_t sn[2];
-                score_tile<D, INT8, F8>(kbuf((j + 1) & 1), qf, l32, g, sn);
+                score_tile<D, INT8, F8, kBiased>(kbuf((j + 1) & 1), qf, l32, g, sn);
 
-                const float negm = -m_run;
+                const float negm = kBiased ? -__builtin_fmaf(kI8Bias, c, m_run) : -m_run;
                 float pv[2][16];
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt)
