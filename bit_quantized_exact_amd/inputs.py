@@ -38,17 +38,30 @@ class Workload:
     outlier_frac: float = 0.0  # fraction of channels whose offset is x10
     via_bf16: bool = False     # draw fp32, round to bf16, then to fp16
     seed: int = 0
+    seq_q: int = 0             # queries per head when they differ from seq (KV-cache
+                               # decode: the last seq_q positions of a seq-token cache)
+
+    @property
+    def n_q(self) -> int:
+        return self.seq_q if self.seq_q else self.seq
 
     @property
     def q_shape(self):
-        return (self.batch, self.heads_q, self.seq, self.head_dim)
+        return (self.batch, self.heads_q, self.n_q, self.head_dim)
 
     @property
     def kv_shape(self):
         return (self.batch, self.heads_kv, self.seq, self.head_dim)
 
     def flops(self) -> float:
-        """4*B*Hq*S^2*D, halved when causal (two contractions of 2*S*S*D each)."""
+        """4*B*Hq*S^2*D, halved when causal (two contractions of 2*S*S*D each).
+        With seq_q queries over a seq-token cache: 4*B*Hq*D per visible
+        (query, key) pair, seq_q*seq pairs, or seq_q*(seq-seq_q) +
+        seq_q*(seq_q+1)/2 when causal (bottom-right aligned)."""
+        if self.seq_q:
+            sq, sk = self.seq_q, self.seq
+            pairs = sq * (sk - sq) + sq * (sq + 1) / 2 if self.causal else sq * sk
+            return 4.0 * self.batch * self.heads_q * self.head_dim * pairs
         f = 4.0 * self.batch * self.heads_q * self.seq * self.seq * self.head_dim
         return f / 2 if self.causal else f
 
@@ -66,6 +79,14 @@ WORKLOADS = {
                           via_bf16=True, seed=2),
     "long_gqa": Workload("long_gqa", 1, 32, 8, 32768, 128, True, 4.0, seed=3),
     "batched_mqa": Workload("batched_mqa", 64, 16, 1, 1024, 128, True, 2.0, seed=4),
+}
+
+
+# KV-cache decode: one new token per sequence (seq_q = 1) attending over an
+# 8192-token cache, LLaMA-style 32 q-heads / 8 kv-heads, a batch of 16.
+DECODE_WORKLOADS = {
+    "decode_gqa": Workload("decode_gqa", 16, 32, 8, 8192, 128, True, 4.0, outlier_frac=0.01,
+                           seed=5, seq_q=1),
 }
 
 

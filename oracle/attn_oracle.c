@@ -35,6 +35,8 @@
  *   - Q is not smoothed.  1/sqrt(D) is applied at dequantisation, not folded
  *     into Q before quantisation.
  *   - Causal means key j is visible to query i iff j <= i (one sequence length).
+ *     With a KV cache (Sq queries, Sk cached keys) the queries are the last Sq
+ *     positions: query i sees keys j <= Sk - Sq + i (bottom-right alignment).
  *   - A row with no visible key (cannot happen for square causal) gives O = 0
  *     and lse = -inf.
  *   - FP8 means OCP E4M3 (bias 7, max 448, no infinities).  FP8 Q/K blocks use
@@ -657,6 +659,125 @@ int oracle_pv8_attention(int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t 
                     m = mt;
                 }
                 for (int c = 0; c < D; ++c) o[c] = acc[c] / l;
+                if (lse) lse[t] = m + log(l);
+            }
+        }
+        free(s); free(acc);
+    }
+    return status;
+}
+
+/* ------------------------------------------------------------------------ */
+/* O1 and O4 with a query length different from the key length: the       */
+/* KV-cache case ([MHA-GQA] §3.4: the keys and values of all earlier       */
+/* tokens are kept, and the queries of the current token(s) attend over    */
+/* them).  Sq queries, Sk >= Sq cached keys; the queries are the LAST Sq    */
+/* positions of the sequence, so under the causal mask query i sees keys   */
+/* j <= (Sk - Sq) + i.  q: [B,Hq,Sq,D]; k, v: [B,Hkv,Sk,D].                */
+/* Written separately from the square functions above (no shared code).    */
+/* ------------------------------------------------------------------------ */
+int oracle_attention_kv(int32_t B, int32_t Hq, int32_t Hkv, int32_t Sq, int32_t Sk, int32_t D,
+                        const uint16_t* q_f16, const uint16_t* k_f16, const uint16_t* v_f16,
+                        const int32_t* kv_map, int32_t causal, double sm_scale,
+                        double* out, double* lse, int32_t nthreads)
+{
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Sk < Sq || D <= 0) return -1;
+    if (check_map(Hq, Hkv, kv_map)) return -4;
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+    int64_t total = (int64_t)B * Hq * Sq;
+    int status = 0;
+#pragma omp parallel
+    {
+        double* s = (double*)malloc((size_t)Sk * sizeof(double));
+        double* acc = (double*)malloc((size_t)D * sizeof(double));
+        if (!s || !acc) {
+#pragma omp atomic write
+            status = -5;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t t = 0; t < total; ++t) {
+                int32_t i = (int32_t)(t % Sq);
+                int64_t bh = t / Sq;
+                int32_t b = (int32_t)(bh / Hq), h = (int32_t)(bh % Hq);
+                int64_t kvbase = ((int64_t)b * Hkv + kv_map[h]) * Sk * D;
+                const uint16_t* qp = q_f16 + t * D;
+                int32_t last = causal ? (Sk - Sq) + i : Sk - 1;   /* last visible key */
+                double m = -INFINITY;
+                for (int32_t j = 0; j <= last; ++j) {
+                    double dot = 0.0;
+                    for (int c = 0; c < D; ++c)
+                        dot += oracle_half_to_double(qp[c]) * oracle_half_to_double(k_f16[kvbase + (int64_t)j * D + c]);
+                    s[j] = dot * sm_scale;
+                    if (s[j] > m) m = s[j];
+                }
+                double l = 0.0;
+                for (int c = 0; c < D; ++c) acc[c] = 0.0;
+                for (int32_t j = 0; j <= last; ++j) {
+                    double p = exp(s[j] - m);
+                    l += p;
+                    for (int c = 0; c < D; ++c) acc[c] += p * oracle_half_to_double(v_f16[kvbase + (int64_t)j * D + c]);
+                }
+                for (int c = 0; c < D; ++c) out[t * D + c] = acc[c] / l;
+                if (lse) lse[t] = m + log(l);
+            }
+        }
+        free(s); free(acc);
+    }
+    return status;
+}
+
+/* O4 for the KV-cache case: INT8 scores S32 * dQ[i/bq] * dK[j/bk] * sm_scale */
+/* with the weights rounded to fp16 for the P.V product (l from unrounded    */
+/* weights).  q_i8 [B,Hq,Sq,D], q_scale [B,Hq,ceil(Sq/bq)]; k_i8 [B,Hkv,Sk,D],*/
+/* k_scale [B,Hkv,ceil(Sk/bk)] (K smoothed with its mean over the Sk cached   */
+/* tokens).                                                                  */
+int oracle_quant_attention_kv(int32_t B, int32_t Hq, int32_t Hkv, int32_t Sq, int32_t Sk, int32_t D,
+                              const int8_t* q_i8, const float* q_scale, int32_t bq,
+                              const int8_t* k_i8, const float* k_scale, int32_t bk,
+                              const uint16_t* v_f16, const int32_t* kv_map, int32_t causal,
+                              double sm_scale, double* out, double* lse, int32_t nthreads)
+{
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Sk < Sq || D <= 0 || bq <= 0 || bk <= 0) return -1;
+    if (check_map(Hq, Hkv, kv_map)) return -4;
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+    int32_t nbq = (Sq + bq - 1) / bq, nbk = (Sk + bk - 1) / bk;
+    int64_t total = (int64_t)B * Hq * Sq;
+    int status = 0;
+#pragma omp parallel
+    {
+        double* s = (double*)malloc((size_t)Sk * sizeof(double));
+        double* acc = (double*)malloc((size_t)D * sizeof(double));
+        if (!s || !acc) {
+#pragma omp atomic write
+            status = -5;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t t = 0; t < total; ++t) {
+                int32_t i = (int32_t)(t % Sq);
+                int64_t bh = t / Sq;
+                int32_t b = (int32_t)(bh / Hq), h = (int32_t)(bh % Hq);
+                int64_t bk_idx = (int64_t)b * Hkv + kv_map[h];
+                const int8_t* qp = q_i8 + t * D;
+                const int8_t* Kh = k_i8 + bk_idx * Sk * D;
+                const uint16_t* Vh = v_f16 + bk_idx * Sk * D;
+                double dq = (double)q_scale[bh * nbq + i / bq];
+                int32_t last = causal ? (Sk - Sq) + i : Sk - 1;
+                double m = -INFINITY;
+                for (int32_t j = 0; j <= last; ++j) {
+                    int64_t dot = 0;
+                    for (int c = 0; c < D; ++c) dot += (int64_t)qp[c] * (int64_t)Kh[(int64_t)j * D + c];
+                    s[j] = (double)dot * dq * (double)k_scale[bk_idx * nbk + j / bk] * sm_scale;
+                    if (s[j] > m) m = s[j];
+                }
+                double l = 0.0;
+                for (int c = 0; c < D; ++c) acc[c] = 0.0;
+                for (int32_t j = 0; j <= last; ++j) {
+                    double p = exp(s[j] - m);
+                    l += p;
+                    double pr = oracle_round_to_half(p);
+                    for (int c = 0; c < D; ++c) acc[c] += pr * oracle_half_to_double(Vh[(int64_t)j * D + c]);
+                }
+                for (int c = 0; c < D; ++c) out[t * D + c] = acc[c] / l;
                 if (lse) lse[t] = m + log(l);
             }
         }

@@ -78,6 +78,11 @@ def lib():
         L.oracle_pv8_attention.argtypes = ([I32] * 5 + [P, P, I32, P, P, I32, P, P, P, I32, D, I32,
                                            I32, P, I32, P, P, I32])
         L.oracle_pv8_attention.restype = ctypes.c_int
+        L.oracle_attention_kv.argtypes = [I32] * 6 + [P, P, P, P, I32, D, P, P, I32]
+        L.oracle_attention_kv.restype = ctypes.c_int
+        L.oracle_quant_attention_kv.argtypes = ([I32] * 6 + [P, P, I32, P, P, I32, P, P, I32, D, P, P,
+                                                I32])
+        L.oracle_quant_attention_kv.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -339,6 +344,63 @@ def pv8_attention(qz, v_codes, v_scale, causal=False, kv_map=None, sm_scale=None
                                     _ptr(out), _ptr(lse) if lse is not None else None, int(nthreads))
     _check(st, "pv8_attention")
     return (out, lse) if with_lse else out
+
+
+# --------------------------------------------------------------------------
+# KV-cache (decode) case: Sq queries over Sk >= Sq cached keys
+# --------------------------------------------------------------------------
+def attention_kv(q, k, v, causal=False, kv_map=None, sm_scale=None, with_lse=False, nthreads=0):
+    """O1 for Sq queries (the last Sq positions) over Sk cached keys.
+    q [B,Hq,Sq,D], k/v [B,Hkv,Sk,D] fp16 -> out [B,Hq,Sq,D] fp64 (and lse)."""
+    B, Hq, Sq, D = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    assert k.shape == (B, Hkv, Sk, D) and v.shape == k.shape
+    m = _map(Hq, Hkv, kv_map)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    out = np.empty((B, Hq, Sq, D), dtype=np.float64)
+    lse = np.empty((B, Hq, Sq), dtype=np.float64) if with_lse else None
+    qb, kb, vb = _bits(q), _bits(k), _bits(v)
+    st = lib().oracle_attention_kv(B, Hq, Hkv, Sq, Sk, D, _ptr(qb), _ptr(kb), _ptr(vb), _ptr(m),
+                                   int(bool(causal)), float(sm_scale), _ptr(out),
+                                   _ptr(lse) if lse is not None else None, int(nthreads))
+    _check(st, "attention_kv")
+    return (out, lse) if with_lse else out
+
+
+def quantize_q(q, bq=BQ):
+    """O3 on Q alone: (q_i8, q_scale [B,Hq,ceil(Sq/bq)])."""
+    return quant_blocks(half_to_float(q), bq)
+
+
+def quant_attention_kv(q_i8, q_scale, kz, v, causal=False, kv_map=None, sm_scale=None,
+                       with_lse=False, bq=BQ, bk=BK, nthreads=0):
+    """O4 for the KV-cache case; kz holds k_i8/k_scale of the Sk cached keys."""
+    qi = np.ascontiguousarray(q_i8)
+    qs = np.ascontiguousarray(q_scale, dtype=np.float32)
+    ki = np.ascontiguousarray(kz["k_i8"])
+    ks = np.ascontiguousarray(kz["k_scale"], dtype=np.float32)
+    B, Hq, Sq, D = qi.shape
+    Hkv, Sk = ki.shape[1], ki.shape[2]
+    m = _map(Hq, Hkv, kv_map)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    out = np.empty((B, Hq, Sq, D), dtype=np.float64)
+    lse = np.empty((B, Hq, Sq), dtype=np.float64) if with_lse else None
+    vb = _bits(v)
+    st = lib().oracle_quant_attention_kv(B, Hq, Hkv, Sq, Sk, D, _ptr(qi), _ptr(qs), bq, _ptr(ki),
+                                         _ptr(ks), bk, _ptr(vb), _ptr(m), int(bool(causal)),
+                                         float(sm_scale), _ptr(out),
+                                         _ptr(lse) if lse is not None else None, int(nthreads))
+    _check(st, "quant_attention_kv")
+    return (out, lse) if with_lse else out
+
+
+def quantize_k_cache(k, bk=BK):
+    """O2 + O3 on the cached keys alone: k_i8, k_scale, k_mean (mean over all Sk tokens)."""
+    mu = k_mean(k)
+    ki, ks = quant_blocks(smooth_k(k, mu), bk)
+    return dict(k_i8=ki, k_scale=ks, k_mean=mu)
 
 
 def max_threads() -> int:
