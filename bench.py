@@ -10,7 +10,9 @@ synthetic fp16 inputs already resident in HBM):
 Outside the timed steps it also times the FP8 alternative (attn_quantize_qk_fp8
 + attn_fwd_fp8) and the 8-bit P.V ablation (attn_quantize_v_fp8 +
 attn_fwd_int8_pv8) and, with the CPU leg, reports their accuracy against the
-exact oracle on the sampled rows.
+exact oracle on the sampled rows; and the KV-cache decode kernels
+(attn_decode_int8, attn_decode_fp16) on the decode workload (batch 16, one
+query per sequence over an 8192-token cache), as GB/s against HBM.
 
 Printed: ONE JSON line.  `value` is the INT8 (SageAttention-form) path's
 attention throughput, quantisation included: FLOP / (t_quantize_k +
@@ -258,10 +260,59 @@ def run_workload(name, steps, warmup, cpu=False, cpu_seconds=15.0):
         "roofline": {k_: (round(v_, 4) if isinstance(v_, float) else v_) for k_, v_ in roof.items()},
         "cpu_baseline": None,
     }
+    rec["paths"]["decode"] = run_decode()
     if cpu:
         rec["cpu_baseline"], rec["parity_sample"] = cpu_baseline(w, q, k, v, o8, o16, cpu_seconds,
                                                                  extra={"fp8_qk": of8, "int8_pv8": opv8})
     return rec
+
+
+def run_decode(name="decode_gqa", reps=20):
+    """KV-cache decode (one query per sequence over a cached context): the
+    INT8 kernel (cache quantised once beforehand) and the FP16 kernel, each
+    timed with HIP events; HBM-bound, so reported as GB/s of algorithmic bytes
+    (the cache read once, Q read and O written once) against 8 TB/s."""
+    import torch
+
+    import bit_quantized_exact_amd as A
+    from bit_quantized_exact_amd.inputs import DECODE_WORKLOADS, make_qkv
+
+    w = DECODE_WORKLOADS[name]
+    q, k, v = make_qkv(w)
+    qd, kd, vd = (torch.from_numpy(x).cuda() for x in (q, k, v))
+    kz = A.quantize_k(kd, with_mean=False)
+    o8, o16 = torch.empty_like(qd), torch.empty_like(qd)
+    ws8 = torch.empty(A.decode_workspace_bytes(A.AttnKvShape(w.batch, w.heads_q, w.heads_kv, w.n_q, w.seq,
+                                                              w.head_dim)), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    f8 = lambda: A.decode_int8(qd, kz, vd, causal=w.causal, out=o8, workspace=ws8)
+    f16 = lambda: A.decode_fp16(qd, kd, vd, causal=w.causal, out=o16, workspace=ws8)
+    res = {}
+    for tag, fn in (("int8", f8), ("fp16", f16)):
+        for _ in range(5):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[tag] = e0.elapsed_time(e1) / reps
+    B, Hq, Hkv, Sq, Sk, D = w.batch, w.heads_q, w.heads_kv, w.n_q, w.seq, w.head_dim
+    qo = 2 * 2 * B * Hq * Sq * D
+    bytes8 = B * Hkv * Sk * D + 2 * B * Hkv * Sk * D + qo + 4 * B * Hkv * math.ceil(Sk / 64)
+    bytes16 = 2 * 2 * B * Hkv * Sk * D + qo
+    out = {"workload": name, "batch": B, "heads_q": Hq, "heads_kv": Hkv, "seq_q": Sq, "seq_kv": Sk,
+           "head_dim": D, "causal": w.causal}
+    for tag, nbytes in (("int8", bytes8), ("fp16", bytes16)):
+        ms = res[tag]
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[tag] = {"us": round(ms * 1e3, 2), "algorithmic_bytes": nbytes, "gbs": round(gbs, 1),
+                    "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                    "tokens_per_s": round(B * Sq / (ms * 1e-3), 1),
+                    "tflops": round(w.flops() / (ms * 1e-3) / 1e12, 2)}
+    out["int8_speedup_over_fp16"] = round(res["fp16"] / res["int8"], 3)
+    return out
 
 
 def cpu_baseline(w, q, k, v, o8, o16, target_s, extra=None):

@@ -17,6 +17,8 @@ kernels.  torch provides device memory and streams.
     attn_fwd_fp8     -> fwd_fp8         E4M3 QK^T, FP16 PV
     attn_quantize_v_fp8 -> quantize_v_fp8   per-channel E4M3 V (transposed)
     attn_fwd_int8_pv8 -> fwd_int8_pv8   INT8 QK^T with 8-bit P and V (ablation)
+    attn_decode_int8 -> decode_int8     KV-cache decode, 8-bit (K from quantize_k on the cache)
+    attn_decode_fp16 -> decode_fp16     KV-cache decode, exact FP16
 
 Sources: SageAttention article ("又快又准，即插即用！清华8比特量化Attention…"),
 技术方案 and its plug-and-play example; "注意力即一切：从 MHA 到 GQA" §2.2-§5.1.
@@ -29,13 +31,13 @@ from typing import Optional
 import torch
 
 from . import _native
-from ._native import AttnShape, lib
+from ._native import AttnKvShape, AttnShape, lib
 
 __all__ = [
     "AttnError", "quant_blocks", "quantize_workspace_bytes", "quantize_qk", "quantize_k",
     "fwd_int8", "fwd_int8_fused_q", "fwd_fp16", "debug_qk_int32", "sageattn", "status_string",
     "quantize_qk_fp8", "fwd_fp8", "v_fp8_stride", "quantize_v_fp8", "fwd_int8_pv8",
-    "AttnShape", "lib",
+    "decode_workspace_bytes", "decode_int8", "decode_fp16", "AttnShape", "AttnKvShape", "lib",
 ]
 
 
@@ -379,4 +381,85 @@ def fwd_int8_pv8(qz: dict, vz: dict, *, causal: bool = False, kv_head_map=None,
     _check(lib().attn_fwd_int8_pv8(ctypes.byref(sh), _ptr(q_i8), _ptr(qs), _ptr(k_i8), _ptr(ks),
                                    _ptr(vt), _ptr(vs), _ptr(out), _ptr(lse), mp, int(bool(causal)),
                                    float(sm_scale or 0.0), _stream(stream)), "attn_fwd_int8_pv8")
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+# --------------------------------------------------------------------------
+# KV-cache (decode) attention
+# --------------------------------------------------------------------------
+def _kv_shape(q: torch.Tensor, k: torch.Tensor) -> AttnKvShape:
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [batch, heads, seq, head_dim]")
+    B, Hq, Sq, D = q.shape
+    if k.shape[0] != B or k.shape[3] != D:
+        raise ValueError(f"k shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    return AttnKvShape(B, Hq, k.shape[1], Sq, k.shape[2], D)
+
+
+def decode_workspace_bytes(shape: AttnKvShape, kv_head_map=None) -> int:
+    _keep, mp = _map_arg(kv_head_map)
+    return int(lib().attn_decode_workspace_bytes(ctypes.byref(shape), mp))
+
+
+def _decode_ws(sh, kv_head_map, workspace, dev):
+    nbytes = decode_workspace_bytes(sh, kv_head_map)
+    if nbytes == 0:
+        raise AttnError(_native.ATTN_EINVAL, "attn_decode_workspace_bytes")
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    return workspace
+
+
+def decode_int8(q: torch.Tensor, kz: dict, v: torch.Tensor, *, causal: bool = True,
+                kv_head_map=None, sm_scale: Optional[float] = None,
+                out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                return_lse: bool = False, q_scale_out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None, stream=None):
+    """8-bit attention of q [B, Hq, Sq, D] (the last Sq positions) over a KV
+    cache: kz = quantize_k(k_cache) (mean over the cached tokens), v the fp16
+    V cache [B, Hkv, Sk, D]."""
+    _dev(q, torch.float16, "q")
+    k_i8 = _dev(kz["k_i8"], torch.int8, "k_i8")
+    ks = _dev(kz["k_scale"], torch.float32, "k_scale")
+    _dev(v, torch.float16, "v")
+    sh = _kv_shape(q, k_i8)
+    if tuple(v.shape) != tuple(k_i8.shape):
+        raise ValueError("v must have the shape of the K cache")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, torch.float16, "out")
+    if return_lse and lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    if q_scale_out is not None:
+        _dev(q_scale_out, torch.float32, "q_scale_out")
+    workspace = _decode_ws(sh, kv_head_map, workspace, q.device)
+    _keep, mp = _map_arg(kv_head_map)
+    _check(lib().attn_decode_int8(ctypes.byref(sh), _ptr(q), _ptr(k_i8), _ptr(ks), _ptr(v), _ptr(out),
+                                  _ptr(lse), _ptr(q_scale_out), mp, int(bool(causal)),
+                                  float(sm_scale or 0.0), _ptr(workspace), _stream(stream)),
+           "attn_decode_int8")
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def decode_fp16(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = True,
+                kv_head_map=None, sm_scale: Optional[float] = None,
+                out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                return_lse: bool = False, workspace: Optional[torch.Tensor] = None, stream=None):
+    """Exact FP16 attention of q [B, Hq, Sq, D] over a K/V cache [B, Hkv, Sk, D]."""
+    _dev(q, torch.float16, "q")
+    _dev(k, torch.float16, "k")
+    _dev(v, torch.float16, "v")
+    sh = _kv_shape(q, k)
+    if tuple(v.shape) != tuple(k.shape):
+        raise ValueError("v must have the shape of the K cache")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, torch.float16, "out")
+    if return_lse and lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    workspace = _decode_ws(sh, kv_head_map, workspace, q.device)
+    _keep, mp = _map_arg(kv_head_map)
+    _check(lib().attn_decode_fp16(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), mp,
+                                  int(bool(causal)), float(sm_scale or 0.0), _ptr(workspace),
+                                  _stream(stream)), "attn_decode_fp16")
     return (out, lse) if (return_lse or lse is not None) else out

@@ -22,7 +22,8 @@ EXPORTED = (
     "attn_quant_blocks", "attn_quantize_workspace_bytes", "attn_quantize_qk", "attn_quantize_k",
     "attn_fwd_int8", "attn_fwd_int8_fused_q", "attn_fwd_fp16", "attn_debug_qk_int32",
     "attn_status_string", "attn_quantize_qk_fp8", "attn_fwd_fp8", "attn_v_fp8_stride",
-    "attn_quantize_v_fp8", "attn_fwd_int8_pv8",
+    "attn_quantize_v_fp8", "attn_fwd_int8_pv8", "attn_decode_workspace_bytes", "attn_decode_int8",
+    "attn_decode_fp16",
 )
 
 
@@ -31,6 +32,14 @@ class AttnShape(ctypes.Structure):
                 ("heads_kv", ctypes.c_int32), ("seq", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32)]
 
+
+class AttnKvShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads_q", ctypes.c_int32),
+                ("heads_kv", ctypes.c_int32), ("seq_q", ctypes.c_int32),
+                ("seq_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32)]
+
+
+ATTN_DECODE_MAX_SEQ_Q = 32
 
 _lib = None
 
@@ -73,6 +82,13 @@ def lib():
     L.attn_quantize_v_fp8.restype = ctypes.c_int
     L.attn_fwd_int8_pv8.argtypes = [SP, P, P, P, P, P, P, P, P, P, ctypes.c_int, F32, P]
     L.attn_fwd_int8_pv8.restype = ctypes.c_int
+    KP = ctypes.POINTER(AttnKvShape)
+    L.attn_decode_workspace_bytes.argtypes = [KP, P]
+    L.attn_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.attn_decode_int8.argtypes = [KP, P, P, P, P, P, P, P, P, ctypes.c_int, F32, P, P]
+    L.attn_decode_int8.restype = ctypes.c_int
+    L.attn_decode_fp16.argtypes = [KP, P, P, P, P, P, P, ctypes.c_int, F32, P, P]
+    L.attn_decode_fp16.restype = ctypes.c_int
     L.attn_status_string.argtypes = [ctypes.c_int]
     L.attn_status_string.restype = ctypes.c_char_p
     _lib = L

@@ -27,6 +27,7 @@ COMMON = [
 SOURCES = {
     "attn_quant.hip": ["-ffp-contract=off"],
     "attn_fwd.hip": [],
+    "attn_decode.hip": [],
     "attn_api.hip": [],
 }
 

@@ -5,6 +5,7 @@
 // nothing: the caller passes every buffer, including the quantisation
 // workspace.
 #include "attn_internal.h"
+#include "decode_geometry.h"
 
 #include <cmath>
 #include <cstring>
@@ -68,6 +69,80 @@ void fill_common(const attn_shape& s, FwdParams* p) {
     p->nkblk = ceil_div(s.seq, kBK);
     p->tile_lo = 0;
     p->ntiles = p->nqt;
+}
+
+int check_kv_shape(const attn_kv_shape* s) {
+    if (!s) return ATTN_EINVAL;
+    if (s->batch <= 0 || s->heads_q <= 0 || s->heads_kv <= 0 || s->seq_q <= 0 || s->seq_kv <= 0 ||
+        s->head_dim <= 0)
+        return ATTN_EINVAL;
+    if (s->seq_q > s->seq_kv) return ATTN_EINVAL;
+    if (s->head_dim != 64 && s->head_dim != 128) return ATTN_EUNSUPPORTED;
+    if (s->heads_q > ATTN_MAX_HEADS || s->heads_kv > ATTN_MAX_HEADS) return ATTN_EUNSUPPORTED;
+    if (s->seq_kv > ATTN_MAX_SEQ || s->seq_q > ATTN_DECODE_MAX_SEQ_Q) return ATTN_EUNSUPPORTED;
+    if (static_cast<long long>(s->batch) * s->heads_kv > 65535LL) return ATTN_EUNSUPPORTED;
+    return ATTN_OK;
+}
+
+// Group tables of the decode launch: q-heads ordered by kv-head, each
+// kv-head's first position and count; returns the largest group.
+int build_groups(const attn_kv_shape& s, const int32_t* user_map, DecParams* p, int* max_group) {
+    uint8_t kvmap[ATTN_MAX_HEADS];
+    if (!user_map) {
+        if (s.heads_q % s.heads_kv != 0) return ATTN_EINVAL;
+        const int grp = s.heads_q / s.heads_kv;
+        for (int h = 0; h < s.heads_q; ++h) kvmap[h] = static_cast<uint8_t>(h / grp);
+    } else {
+        for (int h = 0; h < s.heads_q; ++h) {
+            if (user_map[h] < 0 || user_map[h] >= s.heads_kv) return ATTN_ERANGE;
+            kvmap[h] = static_cast<uint8_t>(user_map[h]);
+        }
+    }
+    int n = 0, mg = 0;
+    for (int k = 0; k < s.heads_kv; ++k) {
+        p->gstart[k] = static_cast<uint16_t>(n);
+        for (int h = 0; h < s.heads_q; ++h)
+            if (kvmap[h] == k) p->horder[n++] = static_cast<uint8_t>(h);
+        p->gcount[k] = static_cast<uint16_t>(n - p->gstart[k]);
+        if (p->gcount[k] > mg) mg = p->gcount[k];
+    }
+    *max_group = mg;
+    return ATTN_OK;
+}
+
+// Validates a decode call and fills everything but the tensor pointers.
+int prepare_decode(const attn_kv_shape* shape, const int32_t* kv_head_map, float sm_scale, DecParams* p,
+                   size_t* ws_bytes) {
+    int st = check_kv_shape(shape);
+    if (st != ATTN_OK) return st;
+    std::memset(p, 0, sizeof(*p));
+    int max_group = 0;
+    if ((st = build_groups(*shape, kv_head_map, p, &max_group)) != ATTN_OK) return st;
+    if ((st = check_scale(sm_scale, shape->head_dim, &p->scale_log2)) != ATTN_OK) return st;
+    const dec::Plan plan = dec::make_plan(shape->batch, shape->heads_kv, shape->seq_q, shape->seq_kv, max_group);
+    if (plan.nchunk > 65535) return ATTN_EUNSUPPORTED;
+    p->B = shape->batch;
+    p->Hq = shape->heads_q;
+    p->Hkv = shape->heads_kv;
+    p->Sq = shape->seq_q;
+    p->Sk = shape->seq_kv;
+    p->nkblk = ceil_div(shape->seq_kv, kBK);
+    p->hpc = plan.hpc;
+    p->nchunk = plan.nchunk;
+    p->ntiles = plan.ntiles;
+    p->tps = plan.tps;
+    p->nsplit = plan.nsplit;
+    *ws_bytes = dec::ws_bytes(dec::partial_rows(shape->batch, shape->heads_kv, plan), shape->head_dim);
+    return ATTN_OK;
+}
+
+void set_workspace(DecParams* p, void* workspace, int D) {
+    const dec::Plan plan{p->hpc, p->nchunk, p->ntiles, p->tps, p->nsplit};
+    const size_t rows = dec::partial_rows(p->B, p->Hkv, plan);
+    char* w = static_cast<char*>(workspace);
+    p->ws_o = reinterpret_cast<float*>(w);
+    p->ws_m = reinterpret_cast<float*>(w + dec::ws_m_offset(rows, D));
+    p->ws_l = reinterpret_cast<float*>(w + dec::ws_l_offset(rows, D));
 }
 
 }  // namespace
@@ -305,6 +380,57 @@ int attn_fwd_int8_pv8(const attn_shape* shape, const int8_t* q_i8, const float* 
     p.k_scale = k_scale;
     p.v_scale = v_scale;
     return launch_fwd(FwdKind::kInt8Pv8, shape->head_dim, causal != 0, p, static_cast<hipStream_t>(stream));
+}
+
+size_t attn_decode_workspace_bytes(const attn_kv_shape* shape, const int32_t* kv_head_map) {
+    DecParams p;
+    size_t bytes = 0;
+    if (prepare_decode(shape, kv_head_map, 0.0f, &p, &bytes) != ATTN_OK) return 0;
+    return bytes;
+}
+
+int attn_decode_int8(const attn_kv_shape* shape, const void* q_f16, const int8_t* k_i8,
+                     const float* k_scale, const void* v_f16, void* o_f16, float* lse,
+                     float* q_scale_out, const int32_t* kv_head_map, int causal, float sm_scale,
+                     void* workspace, void* stream) {
+    DecParams p;
+    size_t bytes = 0;
+    int st = prepare_decode(shape, kv_head_map, sm_scale, &p, &bytes);
+    if (st != ATTN_OK) return st;
+    if (!q_f16 || !k_i8 || !k_scale || !v_f16 || !o_f16 || !workspace) return ATTN_EINVAL;
+    if (!aligned(q_f16, 16) || !aligned(k_i8, 16) || !aligned(v_f16, 16) || !aligned(o_f16, 16) ||
+        !aligned(workspace, 16) || !aligned(k_scale, 4) || (lse && !aligned(lse, 4)) ||
+        (q_scale_out && !aligned(q_scale_out, 4)))
+        return ATTN_EINVAL;
+    p.q = q_f16;
+    p.k = k_i8;
+    p.v = v_f16;
+    p.o = o_f16;
+    p.lse = lse;
+    p.k_scale = k_scale;
+    p.q_scale_out = q_scale_out;
+    set_workspace(&p, workspace, shape->head_dim);
+    return launch_decode(true, shape->head_dim, causal != 0, p, static_cast<hipStream_t>(stream));
+}
+
+int attn_decode_fp16(const attn_kv_shape* shape, const void* q_f16, const void* k_f16,
+                     const void* v_f16, void* o_f16, float* lse, const int32_t* kv_head_map,
+                     int causal, float sm_scale, void* workspace, void* stream) {
+    DecParams p;
+    size_t bytes = 0;
+    int st = prepare_decode(shape, kv_head_map, sm_scale, &p, &bytes);
+    if (st != ATTN_OK) return st;
+    if (!q_f16 || !k_f16 || !v_f16 || !o_f16 || !workspace) return ATTN_EINVAL;
+    if (!aligned(q_f16, 16) || !aligned(k_f16, 16) || !aligned(v_f16, 16) || !aligned(o_f16, 16) ||
+        !aligned(workspace, 16) || (lse && !aligned(lse, 4)))
+        return ATTN_EINVAL;
+    p.q = q_f16;
+    p.k = k_f16;
+    p.v = v_f16;
+    p.o = o_f16;
+    p.lse = lse;
+    set_workspace(&p, workspace, shape->head_dim);
+    return launch_decode(false, shape->head_dim, causal != 0, p, static_cast<hipStream_t>(stream));
 }
 
 const char* attn_status_string(int status) {

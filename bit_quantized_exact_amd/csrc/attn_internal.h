@@ -72,4 +72,26 @@ enum class FwdKind { kFp16, kInt8, kDumpInt8, kInt8FusedQ, kFp8, kInt8Pv8 };
 
 int launch_fwd(FwdKind kind, int head_dim, bool causal, const FwdParams& p, hipStream_t st);
 
+// KV-cache (decode) attention: Sq <= 32 queries per head over Sk cached keys.
+struct DecParams {
+    const void* q;        // fp16 [B,Hq,Sq,D]
+    const void* k;        // int8 or fp16 [B,Hkv,Sk,D]
+    const void* v;        // fp16 [B,Hkv,Sk,D]
+    void* o;              // fp16 [B,Hq,Sq,D]
+    float* lse;           // fp32 [B,Hq,Sq] or null
+    const float* k_scale; // INT8 path: [B,Hkv,nkblk]
+    float* q_scale_out;   // INT8 path: the per-head Q block scales [B,Hq], or null
+    float* ws_o;          // partial results (see decode_geometry.h)
+    float* ws_m;
+    float* ws_l;
+    int B, Hq, Hkv, Sq, Sk, nkblk;
+    int hpc, nchunk, ntiles, tps, nsplit;   // the launch plan
+    float scale_log2;
+    uint16_t gstart[ATTN_MAX_HEADS];  // first position of kv-head k's group in horder
+    uint16_t gcount[ATTN_MAX_HEADS];  // size of that group
+    uint8_t horder[ATTN_MAX_HEADS];   // q-heads ordered by kv-head
+};
+
+int launch_decode(bool int8, int head_dim, bool causal, const DecParams& p, hipStream_t st);
+
 }  // namespace attn

@@ -220,6 +220,52 @@ int attn_fwd_int8_pv8(const attn_shape* shape, const int8_t* q_i8, const float* 
                       const float* v_scale, void* o_f16, float* lse, const int32_t* kv_head_map,
                       int causal, float sm_scale, void* stream);
 
+/* ---- KV-cache (decode) attention ------------------------------------------
+ * [MHA-GQA] §3.4: during generation the keys and values of all earlier tokens
+ * are cached; the queries of the current token(s) attend over the cache.
+ * seq_q queries per head (the LAST seq_q positions of the sequence) attend
+ * over seq_kv >= seq_q cached keys; under the causal mask query i sees keys
+ * j <= seq_kv - seq_q + i (bottom-right alignment).  Layout: Q, O
+ * [batch, heads_q, seq_q, head_dim]; K, V [batch, heads_kv, seq_kv, head_dim];
+ * other conventions as above.  seq_q is at most ATTN_DECODE_MAX_SEQ_Q. */
+#define ATTN_DECODE_MAX_SEQ_Q 32
+
+typedef struct attn_kv_shape {
+    int32_t batch;
+    int32_t heads_q;
+    int32_t heads_kv;
+    int32_t seq_q;     /* 1 .. min(seq_kv, ATTN_DECODE_MAX_SEQ_Q) */
+    int32_t seq_kv;    /* 1 .. ATTN_MAX_SEQ */
+    int32_t head_dim;  /* 64 or 128 */
+} attn_kv_shape;
+
+/* Bytes of device workspace the decode calls need for `shape` and the head map
+ * (per-split partial results: the cache is split over many workgroups whose
+ * partial maxima, sums and outputs are then merged).  0 if the arguments are
+ * invalid. */
+size_t attn_decode_workspace_bytes(const attn_kv_shape* shape, const int32_t* kv_head_map);
+
+/* 8-bit decode ([SA] 技术方案 on a KV cache).  The cached K is smoothed and
+ * quantised by attn_quantize_k called with seq = seq_kv (mean over all cached
+ * tokens, BK-key blocks).  Each head's seq_q query rows form one Q block and
+ * are quantised inside the kernel with the rule of attn_quantize_qk
+ * (a = max|x| over the block, delta = a/127, q = clamp(rint(x*127/a))).
+ *   s[i,j] = (sum_c q_i8[i,c] k_i8[j,c]) * delta_q * k_scale[j/BK] * sm_scale
+ * then the online softmax, P rounded to fp16, P V in FP16 with fp32
+ * accumulation, O stored fp16.
+ * q_scale_out out fp32 [batch, heads_q] (the Q block scales) or NULL;
+ * lse out fp32 [batch, heads_q, seq_q] or NULL; workspace of
+ * attn_decode_workspace_bytes(shape, kv_head_map) bytes, 16-byte aligned. */
+int attn_decode_int8(const attn_kv_shape* shape, const void* q_f16, const int8_t* k_i8,
+                     const float* k_scale, const void* v_f16, void* o_f16, float* lse,
+                     float* q_scale_out, const int32_t* kv_head_map, int causal, float sm_scale,
+                     void* workspace, void* stream);
+
+/* Exact FP16 decode: as attn_fwd_fp16 for seq_q queries over the cache. */
+int attn_decode_fp16(const attn_kv_shape* shape, const void* q_f16, const void* k_f16,
+                     const void* v_f16, void* o_f16, float* lse, const int32_t* kv_head_map,
+                     int causal, float sm_scale, void* workspace, void* stream);
+
 /* Static text for a status code. */
 const char* attn_status_string(int status);
 

@@ -249,3 +249,60 @@ def test_fp8_entry_points_validation():
     assert pv8(scale=float("inf")) == -1
     assert pv8(shape=bad) == -2
     assert pv8(mp=ctypes.cast(badmap, ctypes.c_void_p)) == -4
+
+
+def _kv(B=1, Hq=4, Hkv=2, Sq=1, Sk=256, D=128):
+    return A.AttnKvShape(B, Hq, Hkv, Sq, Sk, D)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("batch", 0, -1), ("heads_q", 0, -1), ("heads_kv", -2, -1), ("seq_q", 0, -1), ("seq_kv", 0, -1),
+    ("head_dim", 0, -1), ("seq_q", 301, -1), ("seq_q", 33, -2), ("head_dim", 80, -2), ("heads_kv", 257, -2),
+    ("seq_kv", (1 << 22) + 1, -2)])
+def test_decode_shape_validation(field, value, code):
+    L = A.lib()
+    sh = _kv(Sk=300)
+    setattr(sh, field, value)
+    assert L.attn_decode_int8(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 1, 0.0,
+                              FAKE, None) == code
+    assert L.attn_decode_fp16(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, None, None, 1, 0.0, FAKE,
+                              None) == code
+    assert L.attn_decode_workspace_bytes(ctypes.byref(sh), None) == 0
+
+
+def test_decode_seq_q_limit():
+    L = A.lib()
+    ok, big = _kv(Sq=32, Sk=64), _kv(Sq=33, Sk=64)
+    assert L.attn_decode_workspace_bytes(ctypes.byref(ok), None) > 0
+    assert L.attn_decode_fp16(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, None, None, 1, 0.0, FAKE,
+                              None) == -2
+
+
+def test_decode_workspace_and_validation():
+    L = A.lib()
+    sh = _kv(B=2, Hq=32, Hkv=8, Sq=1, Sk=8192)
+    n = L.attn_decode_workspace_bytes(ctypes.byref(sh), None)
+    # at least one partial row (D floats + max + sum) per (batch, kv-head, split)
+    assert n >= 2 * 8 * (128 + 2) * 4 and n % 256 == 0
+    assert L.attn_decode_workspace_bytes(None, None) == 0
+    bad = (ctypes.c_int32 * 32)(*([0] * 31 + [8]))
+    assert L.attn_decode_workspace_bytes(ctypes.byref(sh), ctypes.cast(bad, ctypes.c_void_p)) == 0
+    P = ctypes.byref(sh)
+    for i in range(6):
+        args = [FAKE] * 6
+        args[i] = None
+        q, k, ks, v, o, ws = args
+        assert L.attn_decode_int8(P, q, k, ks, v, o, None, None, None, 1, 0.0, ws, None) == -1
+    assert L.attn_decode_int8(P, MISALIGNED, FAKE, FAKE, FAKE, FAKE, None, None, None, 1, 0.0, FAKE,
+                              None) == -1
+    assert L.attn_decode_int8(P, FAKE, FAKE, FAKE + 2, FAKE, FAKE, None, None, None, 1, 0.0, FAKE,
+                              None) == -1
+    assert L.attn_decode_int8(P, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE + 2, None, 1, 0.0, FAKE,
+                              None) == -1
+    assert L.attn_decode_fp16(P, FAKE, FAKE, FAKE, FAKE, None, None, 1, float("nan"), FAKE, None) == -1
+    assert L.attn_decode_fp16(P, FAKE, FAKE, FAKE, FAKE, None, ctypes.cast(bad, ctypes.c_void_p), 1, 0.0,
+                              FAKE, None) == -4
+    assert L.attn_decode_fp16(P, FAKE, FAKE, FAKE, FAKE, None, None, 1, 0.0, MISALIGNED, None) == -1
+    odd = _kv(Hq=6, Hkv=4)
+    assert L.attn_decode_fp16(ctypes.byref(odd), FAKE, FAKE, FAKE, FAKE, None, None, 1, 0.0, FAKE,
+                              None) == -1

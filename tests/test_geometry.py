@@ -24,3 +24,16 @@ def test_forward_kernel_addresses_stay_in_bounds(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stdout[-2000:]
     assert "0 errors" in r.stdout
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
+def test_decode_kernel_addresses_stay_in_bounds(tmp_path):
+    exe = tmp_path / "decode_geometry_check"
+    subprocess.check_call([
+        HIPCC, "-O2", "-std=c++17", "--offload-arch=gfx950",
+        "-I", os.path.join(ROOT, "bit_quantized_exact_amd", "csrc"), "-I", os.path.join(ROOT, "include"),
+        os.path.join(ROOT, "tests", "decode_geometry_check.hip"), "-o", str(exe)],
+        stderr=subprocess.DEVNULL)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout[-2000:]
+    assert "0 errors" in r.stdout
