@@ -251,7 +251,9 @@ void decode_kernel(const DecParams p) {
         const float m_tile = (INT8 ? row_max(mx) - kI8Bias : row_max(mx)) * c;
         if (__ballot(m_tile > m_run + kLazy)) {
             const float m_new = __builtin_fmaxf(m_run, m_tile);
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            // (a row that has seen no key yet has an empty state: alpha = 0 avoids
+            // exp2(-inf - -inf) when the other rows of the wave raise their maximum)
+            const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
             m_run = m_new;
             l_run *= alpha;
 #pragma unroll
@@ -311,41 +313,41 @@ void decode_kernel(const DecParams p) {
 
 // Merge the key ranges: m = max_s m_s, w_s = 2^(m_s - m), l = sum_s w_s l_s,
 // O = sum_s w_s O_s / l (ranges with no visible key have m_s = -inf, w_s = 0).
-// One workgroup per (batch, kv-head, query chunk); 8 threads per query slot.
+// Thread (r, c4): query slot 8 * blockIdx.x + r of one (batch, kv-head,
+// chunk), output columns 4 c4 .. 4 c4 + 3; blocks without a valid slot exit.
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(const DecParams p) {
-    constexpr int PER = D / 8;   // columns per thread
-    const int chunk = blockIdx.x, bkv = blockIdx.y;
+    constexpr int CG = D / 4;            // 4-column groups per row
+    constexpr int RPB = 256 / CG;        // slots per block
+    const int chunk = blockIdx.y, bkv = blockIdx.z;
     const int b = bkv / p.Hkv, kvh = bkv - b * p.Hkv;
-    const int n = threadIdx.x >> 3, part = threadIdx.x & 7;
+    const int c4 = threadIdx.x % CG;
+    const int n = blockIdx.x * RPB + threadIdx.x / CG;
     const dec::Plan plan{p.hpc, p.nchunk, p.ntiles, p.tps, p.nsplit};
     const dec::Slot sl = dec::slot_of(n, chunk, p.hpc, p.Sq, p.gcount[kvh]);
     if (!sl.valid) return;
     const int h = p.horder[p.gstart[kvh] + sl.hh];
+    const size_t row0 = dec::partial_row(bkv, chunk, 0, n, plan);
+    const size_t stride = dec::kSlots;   // rows between consecutive splits of one slot
     float m = -INFINITY;
-    for (int s = 0; s < p.nsplit; ++s) m = __builtin_fmaxf(m, p.ws_m[dec::partial_row(bkv, chunk, s, n, plan)]);
+#pragma unroll 8
+    for (int s = 0; s < p.nsplit; ++s) m = __builtin_fmaxf(m, p.ws_m[row0 + s * stride]);
     float l = 0.0f;
-    float acc[PER];
-#pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] = 0.0f;
+    f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
     for (int s = 0; s < p.nsplit; ++s) {
-        const size_t row = dec::partial_row(bkv, chunk, s, n, plan);
+        const size_t row = row0 + s * stride;
         const float ms = p.ws_m[row];
-        if (ms == -INFINITY) continue;
-        const float w = __builtin_amdgcn_exp2f(ms - m);
+        const float w = ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms - m);
         l += w * p.ws_l[row];
-        const float* o = p.ws_o + row * D + part * PER;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] += w * o[e];
+        acc += w * *reinterpret_cast<const f4*>(p.ws_o + row * D + c4 * 4);
     }
     const float inv = 1.0f / l;
-    _Float16* out = static_cast<_Float16*>(p.o) + ((static_cast<size_t>(b) * p.Hq + h) * p.Sq + sl.i) * D + part * PER;
-#pragma unroll
-    for (int e = 0; e < PER; e += 2) {
-        const h2 v = __builtin_convertvector((f2){acc[e] * inv, acc[e + 1] * inv}, h2);
-        *reinterpret_cast<h2*>(out + e) = v;
-    }
-    if (p.lse && part == 0) p.lse[(static_cast<size_t>(b) * p.Hq + h) * p.Sq + sl.i] = (m + __builtin_log2f(l)) * kLn2;
+    _Float16* out = static_cast<_Float16*>(p.o) + ((static_cast<size_t>(b) * p.Hq + h) * p.Sq + sl.i) * D + c4 * 4;
+    const h2 lo = __builtin_convertvector((f2){acc[0] * inv, acc[1] * inv}, h2);
+    const h2 hi = __builtin_convertvector((f2){acc[2] * inv, acc[3] * inv}, h2);
+    *reinterpret_cast<h4*>(out) = __builtin_shufflevector(lo, hi, 0, 1, 2, 3);
+    if (p.lse && c4 == 0) p.lse[(static_cast<size_t>(b) * p.Hq + h) * p.Sq + sl.i] = (m + __builtin_log2f(l)) * kLn2;
 }
 
 template <int D, bool INT8>
@@ -355,7 +357,11 @@ void launch_decode_d(bool causal, const DecParams& p, hipStream_t st) {
         hipLaunchKernelGGL((decode_kernel<D, INT8, true>), grid, dim3(dec::kThreads), 0, st, p);
     else
         hipLaunchKernelGGL((decode_kernel<D, INT8, false>), grid, dim3(dec::kThreads), 0, st, p);
-    hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(p.nchunk, p.B * p.Hkv), dim3(256), 0, st, p);
+    // only the blocks holding the first hpc*Sq slots can have valid slots
+    const int rpb = 256 / (D / 4);
+    const int used = dec::imin(dec::kSlots, p.hpc * p.Sq);
+    hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(dec::cdiv(used, rpb), p.nchunk, p.B * p.Hkv), dim3(256), 0,
+                       st, p);
 }
 
 }  // namespace

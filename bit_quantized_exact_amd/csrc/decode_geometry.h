@@ -25,7 +25,13 @@ constexpr int kSlots = 32;        // query slots per wave (MFMA N dimension)
 constexpr int kTile = 32;         // keys per tile
 constexpr int kThreads = 64;      // one wave per workgroup
 constexpr int kMaxSq = 32;        // queries per head handled in one wave
-constexpr int kTargetGroups = 2048;  // workgroups a launch aims for (256 CUs x 8)
+#ifndef ATTN_DECODE_TARGET_GROUPS
+#define ATTN_DECODE_TARGET_GROUPS 1024
+#endif
+// workgroups a launch aims for: 4 single-wave workgroups per CU keep enough
+// of the cache in flight (measured: 2 per CU starve the INT8 path, 8 per CU
+// add partial-result traffic and per-workgroup set-up)
+constexpr int kTargetGroups = ATTN_DECODE_TARGET_GROUPS;
 constexpr int kMinTilesPerSplit = 8;
 
 __host__ __device__ inline int imin(int a, int b) { return a < b ? a : b; }

@@ -54,7 +54,7 @@ static void check(int B, int Hq, int Hkv, int Sq, int Sk, int D, const std::vect
     const size_t q_bytes = static_cast<size_t>(B) * Hq * Sq * D * 2;
     const size_t rows_total = partial_rows(B, Hkv, p);
     const int nkblk = (Sk + 63) / 64;
-    std::vector<int> owner(static_cast<size_t>(B) * Hq * Sq, 0);
+    std::vector<int> owner(static_cast<size_t>(B) * Hq * Sq, 0), written(owner.size(), 0);
     for (int elt = 0; elt < 2; ++elt) {   // INT8 (1-byte K) and FP16 (2-byte K)
         const int kelt = elt ? 2 : 1;
         const size_t kv_k_bytes = static_cast<size_t>(B) * Hkv * Sk * D * kelt;
@@ -114,23 +114,31 @@ static void check(int B, int Hq, int Hkv, int Sq, int Sk, int D, const std::vect
                             REQUIRE(static_cast<size_t>(b) * Hq + h < static_cast<size_t>(B) * Hq, "q scale out");
                         }
                     }
-            // combine kernel: 8 threads per slot
+            // combine kernel: D/4 threads per slot, 256/(D/4) slots per block,
+            // blocks over the first hpc*Sq slots
+            const int cg = D / 4, rpb = 256 / cg;
+            const int nblk = cdiv(imin(kSlots, p.hpc * Sq), rpb);
             for (int chunk = 0; chunk < p.nchunk; ++chunk)
-                for (int tid = 0; tid < 256; ++tid) {
-                    const int n = tid >> 3, part = tid & 7;
-                    const Slot sl = slot_of(n, chunk, p.hpc, Sq, gcount[kvh]);
-                    if (!sl.valid) continue;
-                    const int h = horder[gstart[kvh] + sl.hh];
-                    for (int s = 0; s < p.nsplit; ++s) {
-                        const size_t row = partial_row(bkv, chunk, s, n, p);
-                        REQUIRE(row < rows_total && row * D + part * (D / 8) + D / 8 <= rows_total * D, "combine row");
+                for (int bx = 0; bx < nblk; ++bx)
+                    for (int tid = 0; tid < 256; ++tid) {
+                        const int n = bx * rpb + tid / cg, c4 = tid % cg;
+                        REQUIRE(n < kSlots, "combine slot %d", n);
+                        const Slot sl = slot_of(n, chunk, p.hpc, Sq, gcount[kvh]);
+                        if (!sl.valid) continue;
+                        const int h = horder[gstart[kvh] + sl.hh];
+                        for (int s = 0; s < p.nsplit; ++s) {
+                            const size_t row = partial_row(bkv, chunk, 0, n, p) + static_cast<size_t>(s) * kSlots;
+                            REQUIRE(row == partial_row(bkv, chunk, s, n, p), "combine split stride");
+                            REQUIRE(row < rows_total && row * D + c4 * 4 + 4 <= rows_total * D, "combine row");
+                        }
+                        const size_t orow = (static_cast<size_t>(b) * Hq + h) * Sq + sl.i;
+                        REQUIRE(orow < static_cast<size_t>(B) * Hq * Sq, "o row %zu", orow);
+                        if (elt == 0 && c4 == 0 && orow < written.size()) written[orow] += 1;
                     }
-                    const size_t orow = (static_cast<size_t>(b) * Hq + h) * Sq + sl.i;
-                    REQUIRE(orow < static_cast<size_t>(B) * Hq * Sq, "o row %zu", orow);
-                }
         }
     }
     for (size_t r = 0; r < owner.size(); ++r) REQUIRE(owner[r] == 1, "query row %zu owned %d times", r, owner[r]);
+    for (size_t r = 0; r < written.size(); ++r) REQUIRE(written[r] == 1, "output row %zu written %d times", r, written[r]);
     REQUIRE(ws_l_offset(rows_total, D) + rows_total * 4 <= ws_bytes(rows_total, D), "workspace size");
 }
 
