@@ -786,4 +786,118 @@ int oracle_quant_attention_kv(int32_t B, int32_t Hq, int32_t Hkv, int32_t Sq, in
     return status;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Attention under a tile-level mask (the APB page: a FlashAttention       */
+/* kernel whose attention mask has a changed shape, built from an anchor   */
+/* block, passing blocks and the local context).  mask[qt * nkt + kt] for */
+/* query tile qt = i / tq and key tile kt = j / tk:                        */
+/*   0: key j invisible to query i;  1: visible;  2: visible iff j <= i.   */
+/* Exact fp64 (quant == NULL) or the O4 quantised model (quant != NULL:    */
+/* INT8 scores with block scales, weights rounded to fp16 for P.V, l from  */
+/* the unrounded weights).  A row with no visible key gives O = 0 and      */
+/* lse = -inf.  q, k, v share the sequence length S.                       */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    const int8_t* q_i8; const float* q_scale; int32_t bq;
+    const int8_t* k_i8; const float* k_scale; int32_t bk;
+} oracle_quant_in;
+
+static int masked_impl(int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t D,
+                       const uint16_t* q_f16, const uint16_t* k_f16, const uint16_t* v_f16,
+                       const oracle_quant_in* quant, const int32_t* kv_map,
+                       const uint8_t* mask, int32_t tq, int32_t tk, double sm_scale,
+                       double* out, double* lse, int32_t nthreads)
+{
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || D <= 0 || tq <= 0 || tk <= 0) return -1;
+    if (check_map(Hq, Hkv, kv_map)) return -4;
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+    int32_t nkt = (S + tk - 1) / tk;
+    int64_t total = (int64_t)B * Hq * S;
+    int status = 0;
+#pragma omp parallel
+    {
+        double* s = (double*)malloc((size_t)S * sizeof(double));
+        int32_t* vis = (int32_t*)malloc((size_t)S * sizeof(int32_t));
+        double* acc = (double*)malloc((size_t)D * sizeof(double));
+        if (!s || !vis || !acc) {
+#pragma omp atomic write
+            status = -5;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t t = 0; t < total; ++t) {
+                int32_t i = (int32_t)(t % S);
+                int64_t bh = t / S;
+                int32_t b = (int32_t)(bh / Hq), h = (int32_t)(bh % Hq);
+                int64_t kvb = ((int64_t)b * Hkv + kv_map[h]) * S * D;
+                int32_t nv = 0;
+                for (int32_t j = 0; j < S; ++j) {
+                    uint8_t m = mask[(int64_t)(i / tq) * nkt + j / tk];
+                    if (m == 1 || (m == 2 && j <= i)) vis[nv++] = j;
+                }
+                double* o = out + t * D;
+                if (nv == 0) {
+                    for (int c = 0; c < D; ++c) o[c] = 0.0;
+                    if (lse) lse[t] = -INFINITY;
+                    continue;
+                }
+                double mx = -INFINITY;
+                for (int32_t a = 0; a < nv; ++a) {
+                    int32_t j = vis[a];
+                    if (quant) {
+                        const int8_t* qp = quant->q_i8 + t * D;
+                        const int8_t* kp = quant->k_i8 + kvb + (int64_t)j * D;
+                        int64_t dot = 0;
+                        for (int c = 0; c < D; ++c) dot += (int64_t)qp[c] * (int64_t)kp[c];
+                        int32_t nbq = (S + quant->bq - 1) / quant->bq, nbk = (S + quant->bk - 1) / quant->bk;
+                        s[a] = (double)dot * (double)quant->q_scale[bh * nbq + i / quant->bq] *
+                               (double)quant->k_scale[((int64_t)b * Hkv + kv_map[h]) * nbk + j / quant->bk] * sm_scale;
+                    } else {
+                        double dot = 0.0;
+                        for (int c = 0; c < D; ++c)
+                            dot += oracle_half_to_double(q_f16[t * D + c]) *
+                                   oracle_half_to_double(k_f16[kvb + (int64_t)j * D + c]);
+                        s[a] = dot * sm_scale;
+                    }
+                    if (s[a] > mx) mx = s[a];
+                }
+                double l = 0.0;
+                for (int c = 0; c < D; ++c) acc[c] = 0.0;
+                for (int32_t a = 0; a < nv; ++a) {
+                    double p = exp(s[a] - mx);
+                    l += p;
+                    double pw = quant ? oracle_round_to_half(p) : p;
+                    for (int c = 0; c < D; ++c)
+                        acc[c] += pw * oracle_half_to_double(v_f16[kvb + (int64_t)vis[a] * D + c]);
+                }
+                for (int c = 0; c < D; ++c) o[c] = acc[c] / l;
+                if (lse) lse[t] = mx + log(l);
+            }
+        }
+        free(s); free(vis); free(acc);
+    }
+    return status;
+}
+
+int oracle_attention_masked(int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t D,
+                            const uint16_t* q_f16, const uint16_t* k_f16, const uint16_t* v_f16,
+                            const int32_t* kv_map, const uint8_t* mask, int32_t tq, int32_t tk,
+                            double sm_scale, double* out, double* lse, int32_t nthreads)
+{
+    return masked_impl(B, Hq, Hkv, S, D, q_f16, k_f16, v_f16, NULL, kv_map, mask, tq, tk, sm_scale,
+                       out, lse, nthreads);
+}
+
+int oracle_quant_attention_masked(int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t D,
+                                  const int8_t* q_i8, const float* q_scale, int32_t bq,
+                                  const int8_t* k_i8, const float* k_scale, int32_t bk,
+                                  const uint16_t* v_f16, const int32_t* kv_map, const uint8_t* mask,
+                                  int32_t tq, int32_t tk, double sm_scale, double* out, double* lse,
+                                  int32_t nthreads)
+{
+    oracle_quant_in qi = {q_i8, q_scale, bq, k_i8, k_scale, bk};
+    if (bq <= 0 || bk <= 0) return -1;
+    return masked_impl(B, Hq, Hkv, S, D, NULL, NULL, v_f16, &qi, kv_map, mask, tq, tk, sm_scale,
+                       out, lse, nthreads);
+}
+
 int oracle_max_threads(void) { return omp_get_max_threads(); }

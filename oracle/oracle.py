@@ -83,6 +83,11 @@ def lib():
         L.oracle_quant_attention_kv.argtypes = ([I32] * 6 + [P, P, I32, P, P, I32, P, P, I32, D, P, P,
                                                 I32])
         L.oracle_quant_attention_kv.restype = ctypes.c_int
+        L.oracle_attention_masked.argtypes = [I32] * 5 + [P, P, P, P, P, I32, I32, D, P, P, I32]
+        L.oracle_attention_masked.restype = ctypes.c_int
+        L.oracle_quant_attention_masked.argtypes = ([I32] * 5 + [P, P, I32, P, P, I32, P, P, P, I32, I32,
+                                                    D, P, P, I32])
+        L.oracle_quant_attention_masked.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -401,6 +406,57 @@ def quantize_k_cache(k, bk=BK):
     mu = k_mean(k)
     ki, ks = quant_blocks(smooth_k(k, mu), bk)
     return dict(k_i8=ki, k_scale=ks, k_mean=mu)
+
+
+# --------------------------------------------------------------------------
+# tile-level attention masks (APB-style anchor / passing / local blocks)
+# --------------------------------------------------------------------------
+TILE_Q, TILE_K = 128, 64   # mask granularity: query rows x keys per mask entry
+
+
+def attention_masked(q, k, v, mask, kv_map=None, sm_scale=None, with_lse=False, tq=TILE_Q, tk=TILE_K,
+                     nthreads=0):
+    """O1 under a tile mask (0 invisible, 1 visible, 2 visible iff j <= i),
+    mask [ceil(S/tq), ceil(S/tk)] uint8.  Rows with no visible key: O = 0, lse = -inf."""
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    m = _map(Hq, Hkv, kv_map)
+    mk = np.ascontiguousarray(mask, dtype=np.uint8)
+    assert mk.shape == (-(-S // tq), -(-S // tk))
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    out = np.empty((B, Hq, S, D), dtype=np.float64)
+    lse = np.empty((B, Hq, S), dtype=np.float64) if with_lse else None
+    qb, kb, vb = _bits(q), _bits(k), _bits(v)
+    st = lib().oracle_attention_masked(B, Hq, Hkv, S, D, _ptr(qb), _ptr(kb), _ptr(vb), _ptr(m), _ptr(mk),
+                                       tq, tk, float(sm_scale), _ptr(out),
+                                       _ptr(lse) if lse is not None else None, int(nthreads))
+    _check(st, "attention_masked")
+    return (out, lse) if with_lse else out
+
+
+def quant_attention_masked(qz, v, mask, kv_map=None, sm_scale=None, with_lse=False, bq=BQ, bk=BK,
+                           tq=TILE_Q, tk=TILE_K, nthreads=0):
+    """O4 under a tile mask (qz from quantize_qk)."""
+    qi = np.ascontiguousarray(qz["q_i8"])
+    ki = np.ascontiguousarray(qz["k_i8"])
+    qs = np.ascontiguousarray(qz["q_scale"], dtype=np.float32)
+    ks = np.ascontiguousarray(qz["k_scale"], dtype=np.float32)
+    B, Hq, S, D = qi.shape
+    Hkv = ki.shape[1]
+    m = _map(Hq, Hkv, kv_map)
+    mk = np.ascontiguousarray(mask, dtype=np.uint8)
+    assert mk.shape == (-(-S // tq), -(-S // tk))
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    out = np.empty((B, Hq, S, D), dtype=np.float64)
+    lse = np.empty((B, Hq, S), dtype=np.float64) if with_lse else None
+    vb = _bits(v)
+    st = lib().oracle_quant_attention_masked(B, Hq, Hkv, S, D, _ptr(qi), _ptr(qs), bq, _ptr(ki), _ptr(ks), bk,
+                                             _ptr(vb), _ptr(m), _ptr(mk), tq, tk, float(sm_scale), _ptr(out),
+                                             _ptr(lse) if lse is not None else None, int(nthreads))
+    _check(st, "quant_attention_masked")
+    return (out, lse) if with_lse else out
 
 
 def max_threads() -> int:
