@@ -19,6 +19,8 @@ kernels.  torch provides device memory and streams.
     attn_fwd_int8_pv8 -> fwd_int8_pv8   INT8 QK^T with 8-bit P and V (ablation)
     attn_decode_int8 -> decode_int8     KV-cache decode, 8-bit (K from quantize_k on the cache)
     attn_decode_fp16 -> decode_fp16     KV-cache decode, exact FP16
+    attn_block_mask_* -> block_mask_tiles / apb_block_mask / block_mask_csr   tile masks
+    attn_fwd_fp16_masked / attn_fwd_int8_masked -> fwd_fp16_masked / fwd_int8_masked
 
 Sources: SageAttention article ("又快又准，即插即用！清华8比特量化Attention…"),
 技术方案 and its plug-and-play example; "注意力即一切：从 MHA 到 GQA" §2.2-§5.1.
@@ -37,7 +39,8 @@ __all__ = [
     "AttnError", "quant_blocks", "quantize_workspace_bytes", "quantize_qk", "quantize_k",
     "fwd_int8", "fwd_int8_fused_q", "fwd_fp16", "debug_qk_int32", "sageattn", "status_string",
     "quantize_qk_fp8", "fwd_fp8", "v_fp8_stride", "quantize_v_fp8", "fwd_int8_pv8",
-    "decode_workspace_bytes", "decode_int8", "decode_fp16", "AttnShape", "AttnKvShape", "lib",
+    "decode_workspace_bytes", "decode_int8", "decode_fp16", "block_mask_tiles", "apb_block_mask",
+    "block_mask_csr", "fwd_fp16_masked", "fwd_int8_masked", "AttnShape", "AttnKvShape", "lib",
 ]
 
 
@@ -462,4 +465,98 @@ def decode_fp16(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bo
     _check(lib().attn_decode_fp16(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), mp,
                                   int(bool(causal)), float(sm_scale or 0.0), _ptr(workspace),
                                   _stream(stream)), "attn_decode_fp16")
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+# --------------------------------------------------------------------------
+# tile-level attention masks (APB-style anchor / passing / local)
+# --------------------------------------------------------------------------
+def block_mask_tiles(seq: int):
+    nq, nk = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().attn_block_mask_tiles(int(seq), ctypes.byref(nq), ctypes.byref(nk)), "attn_block_mask_tiles")
+    return nq.value, nk.value
+
+
+def apb_block_mask(seq: int, anchor: int, passing: int):
+    """Host tile mask (numpy uint8 [q_tiles, k_tiles]) of the APB layout."""
+    import numpy as np
+    nq, nk = block_mask_tiles(seq)
+    m = np.zeros((nq, nk), dtype=np.uint8)
+    _check(lib().attn_block_mask_apb(int(seq), int(anchor), int(passing), m.ctypes.data_as(ctypes.c_void_p)),
+           "attn_block_mask_apb")
+    return m
+
+
+def block_mask_csr(seq: int, mask, device="cuda"):
+    """The tile list of a dense host tile mask, copied to the device:
+    dict(row_ptr, cols, nnz)."""
+    import numpy as np
+    nq, nk = block_mask_tiles(seq)
+    m = np.ascontiguousarray(mask, dtype=np.uint8)
+    if m.shape != (nq, nk):
+        raise ValueError(f"mask must be [{nq}, {nk}] for seq {seq}")
+    row_ptr = np.zeros(nq + 1, dtype=np.int32)
+    cols = np.zeros(max(1, nq * nk), dtype=np.int32)
+    nnz = ctypes.c_int32()
+    _check(lib().attn_block_mask_csr(int(seq), m.ctypes.data_as(ctypes.c_void_p),
+                                     row_ptr.ctypes.data_as(ctypes.c_void_p),
+                                     cols.ctypes.data_as(ctypes.c_void_p), ctypes.byref(nnz)),
+           "attn_block_mask_csr")
+    return dict(row_ptr=torch.from_numpy(row_ptr).to(device),
+                cols=torch.from_numpy(cols[:max(1, nnz.value)].copy()).to(device), nnz=nnz.value, seq=int(seq))
+
+
+def _csr_args(csr, seq):
+    if csr.get("seq") != seq:
+        raise ValueError("the mask list was built for another sequence length")
+    rp = _dev(csr["row_ptr"], torch.int32, "row_ptr")
+    cols = _dev(csr["cols"], torch.int32, "cols")
+    return rp, cols, int(csr["nnz"])
+
+
+def fwd_fp16_masked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, csr: dict, *, kv_head_map=None,
+                    sm_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None, return_lse: bool = False, stream=None):
+    """Exact FP16 forward under a tile mask (csr from block_mask_csr)."""
+    _dev(q, torch.float16, "q")
+    _dev(k, torch.float16, "k")
+    _dev(v, torch.float16, "v")
+    sh = _shape(q, k)
+    if tuple(v.shape) != tuple(k.shape):
+        raise ValueError("v must have the shape of k")
+    rp, cols, nnz = _csr_args(csr, sh.seq)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, torch.float16, "out")
+    if return_lse and lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    _keep, mp = _map_arg(kv_head_map)
+    _check(lib().attn_fwd_fp16_masked(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), mp,
+                                      _ptr(rp), _ptr(cols), nnz, float(sm_scale or 0.0), _stream(stream)),
+           "attn_fwd_fp16_masked")
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def fwd_int8_masked(qz: dict, v: torch.Tensor, csr: dict, *, kv_head_map=None,
+                    sm_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None, return_lse: bool = False, stream=None):
+    """8-bit forward (quantize_qk output) under a tile mask."""
+    q_i8 = _dev(qz["q_i8"], torch.int8, "q_i8")
+    k_i8 = _dev(qz["k_i8"], torch.int8, "k_i8")
+    qs = _dev(qz["q_scale"], torch.float32, "q_scale")
+    ks = _dev(qz["k_scale"], torch.float32, "k_scale")
+    _dev(v, torch.float16, "v")
+    sh = _shape(q_i8, k_i8)
+    if tuple(v.shape) != tuple(k_i8.shape):
+        raise ValueError("v must have the shape of k")
+    rp, cols, nnz = _csr_args(csr, sh.seq)
+    if out is None:
+        out = torch.empty(q_i8.shape, dtype=torch.float16, device=v.device)
+    _dev(out, torch.float16, "out")
+    if return_lse and lse is None:
+        lse = torch.empty(q_i8.shape[:3], dtype=torch.float32, device=v.device)
+    _keep, mp = _map_arg(kv_head_map)
+    _check(lib().attn_fwd_int8_masked(ctypes.byref(sh), _ptr(q_i8), _ptr(qs), _ptr(k_i8), _ptr(ks), _ptr(v),
+                                      _ptr(out), _ptr(lse), mp, _ptr(rp), _ptr(cols), nnz,
+                                      float(sm_scale or 0.0), _stream(stream)), "attn_fwd_int8_masked")
     return (out, lse) if (return_lse or lse is not None) else out

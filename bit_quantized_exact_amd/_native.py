@@ -23,7 +23,8 @@ EXPORTED = (
     "attn_fwd_int8", "attn_fwd_int8_fused_q", "attn_fwd_fp16", "attn_debug_qk_int32",
     "attn_status_string", "attn_quantize_qk_fp8", "attn_fwd_fp8", "attn_v_fp8_stride",
     "attn_quantize_v_fp8", "attn_fwd_int8_pv8", "attn_decode_workspace_bytes", "attn_decode_int8",
-    "attn_decode_fp16",
+    "attn_decode_fp16", "attn_block_mask_tiles", "attn_block_mask_apb", "attn_block_mask_csr",
+    "attn_fwd_fp16_masked", "attn_fwd_int8_masked",
 )
 
 
@@ -89,6 +90,16 @@ def lib():
     L.attn_decode_int8.restype = ctypes.c_int
     L.attn_decode_fp16.argtypes = [KP, P, P, P, P, P, P, ctypes.c_int, F32, P, P]
     L.attn_decode_fp16.restype = ctypes.c_int
+    L.attn_block_mask_tiles.argtypes = [I32, P, P]
+    L.attn_block_mask_tiles.restype = ctypes.c_int
+    L.attn_block_mask_apb.argtypes = [I32, I32, I32, P]
+    L.attn_block_mask_apb.restype = ctypes.c_int
+    L.attn_block_mask_csr.argtypes = [I32, P, P, P, P]
+    L.attn_block_mask_csr.restype = ctypes.c_int
+    L.attn_fwd_fp16_masked.argtypes = [SP, P, P, P, P, P, P, P, P, I32, F32, P]
+    L.attn_fwd_fp16_masked.restype = ctypes.c_int
+    L.attn_fwd_int8_masked.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, I32, F32, P]
+    L.attn_fwd_int8_masked.restype = ctypes.c_int
     L.attn_status_string.argtypes = [ctypes.c_int]
     L.attn_status_string.restype = ctypes.c_char_p
     _lib = L

@@ -7,6 +7,7 @@
 #include "attn_internal.h"
 #include "decode_geometry.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 
@@ -431,6 +432,109 @@ int attn_decode_fp16(const attn_kv_shape* shape, const void* q_f16, const void* 
     p.lse = lse;
     set_workspace(&p, workspace, shape->head_dim);
     return launch_decode(false, shape->head_dim, causal != 0, p, static_cast<hipStream_t>(stream));
+}
+
+int attn_block_mask_tiles(int32_t seq, int32_t* q_tiles, int32_t* k_tiles) {
+    if (seq <= 0 || seq > ATTN_MAX_SEQ) return ATTN_EINVAL;
+    if (q_tiles) *q_tiles = ceil_div(seq, ATTN_MASK_TILE_Q);
+    if (k_tiles) *k_tiles = ceil_div(seq, ATTN_MASK_TILE_K);
+    return ATTN_OK;
+}
+
+int attn_block_mask_apb(int32_t seq, int32_t anchor, int32_t passing, uint8_t* mask) {
+    if (!mask || seq <= 0 || seq > ATTN_MAX_SEQ || anchor < 0 || passing < 0) return ATTN_EINVAL;
+    if (anchor % ATTN_MASK_TILE_Q || passing % ATTN_MASK_TILE_Q || anchor + passing > seq) return ATTN_EINVAL;
+    const int nqt = ceil_div(seq, ATTN_MASK_TILE_Q), nkt = ceil_div(seq, ATTN_MASK_TILE_K);
+    for (int qt = 0; qt < nqt; ++qt) {
+        const int i0 = qt * ATTN_MASK_TILE_Q, i1 = std::min(seq, i0 + ATTN_MASK_TILE_Q) - 1;
+        const bool passing_rows = i0 >= anchor && i0 < anchor + passing;
+        for (int kt = 0; kt < nkt; ++kt) {
+            const int j0 = kt * ATTN_MASK_TILE_K, j1 = std::min(seq, j0 + ATTN_MASK_TILE_K) - 1;
+            uint8_t m = 0;
+            if (!passing_rows) m = j1 <= i0 ? 1 : (j0 <= i1 ? 2 : 0);   // causal over [anchor|passing|local]
+            mask[static_cast<size_t>(qt) * nkt + kt] = m;
+        }
+    }
+    return ATTN_OK;
+}
+
+int attn_block_mask_csr(int32_t seq, const uint8_t* mask, int32_t* row_ptr, int32_t* cols, int32_t* nnz) {
+    if (!mask || !row_ptr || !cols || !nnz || seq <= 0 || seq > ATTN_MAX_SEQ) return ATTN_EINVAL;
+    const int nqt = ceil_div(seq, ATTN_MASK_TILE_Q), nkt = ceil_div(seq, ATTN_MASK_TILE_K);
+    for (size_t e = 0; e < static_cast<size_t>(nqt) * nkt; ++e)
+        if (mask[e] > 2) return ATTN_EINVAL;
+    int n = 0;
+    for (int qt = 0; qt < nqt; ++qt) {
+        row_ptr[qt] = n;
+        const int i0 = qt * ATTN_MASK_TILE_Q, i1 = std::min(seq, i0 + ATTN_MASK_TILE_Q) - 1;
+        for (int kt = 0; kt < nkt; ++kt) {
+            int m = mask[static_cast<size_t>(qt) * nkt + kt];
+            const int j0 = kt * ATTN_MASK_TILE_K, j1 = std::min(seq, j0 + ATTN_MASK_TILE_K) - 1;
+            if (m == 2 && j1 <= i0) m = 1;   // every key precedes every query of the tile
+            if (m == 2 && j0 > i1) m = 0;    // no key precedes any query of the tile
+            if (m) cols[n++] = (kt << 2) | m;
+        }
+    }
+    row_ptr[nqt] = n;
+    *nnz = n;
+    return ATTN_OK;
+}
+
+int attn_fwd_fp16_masked(const attn_shape* shape, const void* q_f16, const void* k_f16, const void* v_f16,
+                         void* o_f16, float* lse, const int32_t* kv_head_map, const int32_t* mask_row_ptr,
+                         const int32_t* mask_cols, int32_t mask_nnz, float sm_scale, void* stream) {
+    int st = check_shape(shape);
+    if (st != ATTN_OK) return st;
+    if (!q_f16 || !k_f16 || !v_f16 || !o_f16 || !mask_row_ptr || mask_nnz < 0 || (mask_nnz > 0 && !mask_cols))
+        return ATTN_EINVAL;
+    if (!aligned(q_f16, 16) || !aligned(k_f16, 16) || !aligned(v_f16, 16) || !aligned(o_f16, 16) ||
+        (lse && !aligned(lse, 4)) || !aligned(mask_row_ptr, 4) || !aligned(mask_cols, 4))
+        return ATTN_EINVAL;
+    FwdParams p;
+    std::memset(&p, 0, sizeof(p));
+    if ((st = build_map(*shape, kv_head_map, &p)) != ATTN_OK) return st;
+    if ((st = check_scale(sm_scale, shape->head_dim, &p.scale_log2)) != ATTN_OK) return st;
+    fill_common(*shape, &p);
+    p.q = q_f16;
+    p.k = k_f16;
+    p.v = v_f16;
+    p.o = o_f16;
+    p.lse = lse;
+    p.mask_rowptr = mask_row_ptr;
+    p.mask_cols = mask_cols;
+    p.mask_nnz = mask_nnz;
+    return launch_fwd(FwdKind::kFp16Mask, shape->head_dim, false, p, static_cast<hipStream_t>(stream));
+}
+
+int attn_fwd_int8_masked(const attn_shape* shape, const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                         const float* k_scale, const void* v_f16, void* o_f16, float* lse,
+                         const int32_t* kv_head_map, const int32_t* mask_row_ptr, const int32_t* mask_cols,
+                         int32_t mask_nnz, float sm_scale, void* stream) {
+    int st = check_shape(shape);
+    if (st != ATTN_OK) return st;
+    if (!q_i8 || !q_scale || !k_i8 || !k_scale || !v_f16 || !o_f16 || !mask_row_ptr || mask_nnz < 0 ||
+        (mask_nnz > 0 && !mask_cols))
+        return ATTN_EINVAL;
+    if (!aligned(q_i8, 16) || !aligned(k_i8, 16) || !aligned(v_f16, 16) || !aligned(o_f16, 16) ||
+        !aligned(q_scale, 4) || !aligned(k_scale, 4) || (lse && !aligned(lse, 4)) || !aligned(mask_row_ptr, 4) ||
+        !aligned(mask_cols, 4))
+        return ATTN_EINVAL;
+    FwdParams p;
+    std::memset(&p, 0, sizeof(p));
+    if ((st = build_map(*shape, kv_head_map, &p)) != ATTN_OK) return st;
+    if ((st = check_scale(sm_scale, shape->head_dim, &p.scale_log2)) != ATTN_OK) return st;
+    fill_common(*shape, &p);
+    p.q = q_i8;
+    p.k = k_i8;
+    p.v = v_f16;
+    p.o = o_f16;
+    p.lse = lse;
+    p.q_scale = q_scale;
+    p.k_scale = k_scale;
+    p.mask_rowptr = mask_row_ptr;
+    p.mask_cols = mask_cols;
+    p.mask_nnz = mask_nnz;
+    return launch_fwd(FwdKind::kInt8Mask, shape->head_dim, false, p, static_cast<hipStream_t>(stream));
 }
 
 const char* attn_status_string(int status) {

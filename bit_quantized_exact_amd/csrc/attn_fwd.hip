@@ -179,12 +179,14 @@ __device__ __forceinline__ void score_tile(const char* ks, const typename Cfg<D,
 
 using geom::key_offset;
 
-template <int D, bool INT8, bool CAUSAL, bool DUMP, bool QF16 = false, bool F8 = false, bool PV8 = false>
+template <int D, bool INT8, bool CAUSAL, bool DUMP, bool QF16 = false, bool F8 = false, bool PV8 = false,
+          bool BMASK = false>
 __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(const FwdParams p) {
     static_assert(!QF16 || (INT8 && !DUMP), "in-kernel Q quantisation is an INT8 forward variant");
     static_assert(!F8 || (INT8 && !DUMP && !QF16 && !PV8), "FP8 scores: standalone-quantised Q/K");
     static_assert(!PV8 || (INT8 && !DUMP && !QF16 && !F8), "8-bit P.V: INT8 Q/K");
+    static_assert(!BMASK || (!CAUSAL && !DUMP && !QF16 && !F8 && !PV8), "tile masks: FP16 or two-call INT8");
     using C = Cfg<D, INT8, F8, PV8>;
     typedef typename C::qfrag_t qfrag_t;
     typedef typename C::acc_t acc_t;
@@ -213,8 +215,36 @@ void fwd_kernel(const FwdParams p) {
     const size_t bhq = static_cast<size_t>(b) * p.Hq + h;
     const size_t bhk = static_cast<size_t>(b) * p.Hkv + kvh;
 
-    const int nkt = geom::block_key_tiles(S, q0, CAUSAL);      // key tiles of the block
-    const int nkt_w = geom::wave_key_tiles(nkt, qw0, CAUSAL);  // key tiles this wave needs
+    // Tile-mask variant (the APB page's FlashAttention kernel with a changed
+    // mask shape): the key tiles of this query tile come from its run of the
+    // mask list, in list order; a query tile with an empty run has no visible
+    // key (O = 0, lse = -inf).
+    geom::MaskRow mrow{0, 0};
+    if constexpr (BMASK) {
+        mrow = geom::mask_row(p.mask_rowptr[qt], p.mask_rowptr[qt + 1], p.mask_nnz, p.nkblk);
+        if (mrow.count == 0) {
+            if (qi < S) {
+                _Float16* orow = static_cast<_Float16*>(p.o) + (bhq * S + static_cast<size_t>(qi)) * D;
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                    for (int j4 = 0; j4 < 4; ++j4) *reinterpret_cast<h4*>(orow + geom::o_column(dt, j4, g)) = h4{};
+                if (p.lse && g == 0) p.lse[bhq * S + qi] = -INFINITY;
+            }
+            return;
+        }
+    }
+    // first key of the tile at list position pos (BMASK), else tile pos itself
+    auto tile_row = [&](int pos) -> int {
+        if constexpr (BMASK) return geom::mask_entry_tile(p.mask_cols[geom::mask_entry_index(mrow, pos)], p.nkblk) * kBN;
+        else return pos * kBN;
+    };
+    auto tile_type = [&](int pos) -> int {
+        if constexpr (BMASK) return geom::mask_entry_type(p.mask_cols[geom::mask_entry_index(mrow, pos)]);
+        else return CAUSAL ? 2 : 1;
+    };
+    const int nkt = BMASK ? mrow.count : geom::block_key_tiles(S, q0, CAUSAL);      // key tiles of the block
+    const int nkt_w = BMASK ? nkt : geom::wave_key_tiles(nkt, qw0, CAUSAL);         // key tiles this wave needs
 
     // ---- K / V staging: each thread moves KPT (VPT) 16-byte chunks per tile.
     // Rows past the sequence are read from row S-1 (always in bounds) and
@@ -297,7 +327,7 @@ void fwd_kernel(const FwdParams p) {
 
     // The first K tile's loads are issued before Q is read and quantised,
     // so the two latencies overlap.
-    if constexpr (!DUMP) gload_k(0, kreg[0]);
+    if constexpr (!DUMP) gload_k(tile_row(0), kreg[0]);
 
     // ---- Q fragment (B operand of S^T = K Q^T), kept in VGPRs.  Rows past
     // the sequence read the last row; they are never stored.
@@ -405,13 +435,13 @@ void fwd_kernel(const FwdParams p) {
         sstore_k(0, kreg[0]);
         __syncthreads();
         score_tile<D, INT8, F8, kBiased>(kbuf(0), qf, l32, g, sc);
-        gload_k(kBN, kreg[0]);
-        gload_v(0, vreg[0]);
+        gload_k(tile_row(1), kreg[0]);
+        gload_v(tile_row(0), vreg[0]);
         sstore_k(1, kreg[0]);
         sstore_v(0, vreg[0]);
         if constexpr (DEPTH == 2) {
-            gload_k(2 * kBN, kreg[DEPTH - 1]);
-            gload_v(kBN, vreg[DEPTH - 1]);
+            gload_k(tile_row(2), kreg[DEPTH - 1]);
+            gload_v(tile_row(1), vreg[DEPTH - 1]);
         }
         __syncthreads();
 
@@ -424,13 +454,13 @@ void fwd_kernel(const FwdParams p) {
         auto step = [&](int j, auto ls_tag) {
             constexpr int LS = decltype(ls_tag)::value;
             constexpr int SS = DEPTH == 2 ? 1 - LS : LS;
-            const int n0 = j * kBN;
-            gload_k(geom::k_load_row<DEPTH>(j), kreg[LS]);
-            gload_v(geom::v_load_row<DEPTH>(j), vreg[LS]);
+            const int n0 = tile_row(j);
+            gload_k(BMASK ? tile_row(j + 1 + DEPTH) : geom::k_load_row<DEPTH>(j), kreg[LS]);
+            gload_v(BMASK ? tile_row(j + DEPTH) : geom::v_load_row<DEPTH>(j), vreg[LS]);
             if (j < nkt_w) {
                 // scores in log2 units: s * c with c = (dQ dK) sm_scale log2(e)
                 float c = p.scale_log2;
-                if constexpr (INT8) c = fmaxf(qscale * kscale[bhk * p.nkblk + j] * p.scale_log2, FLT_MIN);
+                if constexpr (INT8) c = fmaxf(qscale * kscale[bhk * p.nkblk + (BMASK ? n0 / kBN : j)] * p.scale_log2, FLT_MIN);
                 float sv[2][16];
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt)
@@ -441,8 +471,12 @@ void fwd_kernel(const FwdParams p) {
                         if constexpr (kBiased) sv[mt][r] = __int_as_float(static_cast<int>(sc[mt][r]));
                         else sv[mt][r] = static_cast<float>(sc[mt][r]);
                     }
-                if (tile_needs_mask(n0)) {
-                    const int lim = mask_limit(n0);
+                const int ty = tile_type(j);
+                const bool needs = BMASK ? (n0 + kBN > S || ty == 0 || (ty == 2 && n0 + kBN - 1 > qw0))
+                                         : tile_needs_mask(n0);
+                if (needs) {
+                    const int lim = !BMASK ? mask_limit(n0)
+                                           : ty == 0 ? -kBN : geom::mask_limit(n0, S, qi, g, ty == 2);
 #pragma unroll
                     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -459,7 +493,9 @@ void fwd_kernel(const FwdParams p) {
                 // (8-bit P needs p <= 1: no lazy headroom there)
                 if (__ballot(m_tile > m_run + (PV8 ? 0.0f : kLazy))) {
                     const float m_new = fmaxf(m_run, m_tile);
-                    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                    // (with tile masks a row may have seen no key yet: its state is
+                    // empty, alpha = 0 avoids exp2(-inf - -inf))
+                    const float alpha = BMASK && m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
                     m_run = m_new;
                     l_run *= alpha;
 #pragma unroll
@@ -470,7 +506,8 @@ void fwd_kernel(const FwdParams p) {
                 acc_t sn[2];
                 score_tile<D, INT8, F8, kBiased>(kbuf((j + 1) & 1), qf, l32, g, sn);
 
-                const float negm = kBiased ? -__builtin_fmaf(kI8Bias, c, m_run) : -m_run;
+                const float m_eff = BMASK && m_run == -INFINITY ? 0.0f : m_run;   // (masked rows: weights 0)
+                const float negm = kBiased ? -__builtin_fmaf(kI8Bias, c, m_eff) : -m_eff;
                 float pv[2][16];
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt)
@@ -558,7 +595,8 @@ void fwd_kernel(const FwdParams p) {
         if constexpr (QF16)
             if (p.q_scale_out && tid == 0) p.q_scale_out[bhq * p.nqblk + qt] = qscale_fused;
         const float l_tot = row_sum(l_run);
-        const float inv = 1.0f / l_tot;
+        // (a row of a tile-masked query tile may see no key: O = 0, lse = -inf)
+        const float inv = BMASK && !(l_tot > 0.0f) ? 0.0f : 1.0f / l_tot;
         if (qi < S) {
             _Float16* orow = static_cast<_Float16*>(p.o) + (bhq * S + static_cast<size_t>(qi)) * D;
             if constexpr (PV8) {
@@ -586,10 +624,12 @@ void fwd_kernel(const FwdParams p) {
     }
 }
 
-template <int D, bool INT8, bool CAUSAL, bool DUMP, bool QF16 = false, bool F8 = false, bool PV8 = false>
+template <int D, bool INT8, bool CAUSAL, bool DUMP, bool QF16 = false, bool F8 = false, bool PV8 = false,
+          bool BMASK = false>
 void launch_one(const FwdParams& p, hipStream_t st) {
     const int blocks = p.B * p.Hq * p.ntiles;
-    hipLaunchKernelGGL((fwd_kernel<D, INT8, CAUSAL, DUMP, QF16, F8, PV8>), dim3(blocks), dim3(kFwdThreads), 0, st, p);
+    hipLaunchKernelGGL((fwd_kernel<D, INT8, CAUSAL, DUMP, QF16, F8, PV8, BMASK>), dim3(blocks), dim3(kFwdThreads), 0,
+                       st, p);
 }
 
 template <int D>
@@ -614,6 +654,12 @@ void launch_d(FwdKind kind, bool causal, const FwdParams& p, hipStream_t st) {
         case FwdKind::kInt8Pv8:
             causal ? launch_one<D, true, true, false, false, false, true>(p, st)
                    : launch_one<D, true, false, false, false, false, true>(p, st);
+            break;
+        case FwdKind::kFp16Mask:
+            launch_one<D, false, false, false, false, false, false, true>(p, st);
+            break;
+        case FwdKind::kInt8Mask:
+            launch_one<D, true, false, false, false, false, false, true>(p, st);
             break;
     }
 }

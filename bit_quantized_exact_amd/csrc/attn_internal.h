@@ -19,6 +19,7 @@ constexpr int kBK = 64;
 // workgroup and one K scale covers a key tile.
 constexpr int kBM = 128;
 constexpr int kBN = 64;
+static_assert(ATTN_MASK_TILE_Q == kBM && ATTN_MASK_TILE_K == kBN, "tile masks use the forward tiles");
 constexpr int kFwdThreads = 256;
 
 // K column sums: tokens per partial-sum chunk.
@@ -57,6 +58,9 @@ struct FwdParams {
     int32_t* s_out;       // score dump: [B,Hq,ntiles*BM,S]
     float* q_scale_out;   // fused-Q INT8 path: the Q block scales, [B,Hq,nqblk], or null
     const float* v_scale; // 8-bit P.V path: per-channel V scales [B,Hkv,D]
+    const int32_t* mask_rowptr;  // tile-mask paths: [nqt + 1] list offsets per query tile
+    const int32_t* mask_cols;    // [mask_nnz] entries (key tile << 2) | type
+    int mask_nnz;
     int B, Hq, Hkv, S;
     int nqt;              // query tiles in the sequence
     int nqblk, nkblk;     // scale blocks per (b, head)
@@ -68,7 +72,8 @@ struct FwdParams {
 
 // kFp8: E4M3 Q/K codes (v_mfma_f32_32x32x64_f8f6f4), FP16 P.V.
 // kInt8Pv8: INT8 Q/K, E4M3 P and per-channel E4M3 V (transposed tiles).
-enum class FwdKind { kFp16, kInt8, kDumpInt8, kInt8FusedQ, kFp8, kInt8Pv8 };
+// kFp16Mask / kInt8Mask: the FP16 / INT8 forward under a tile-mask list.
+enum class FwdKind { kFp16, kInt8, kDumpInt8, kInt8FusedQ, kFp8, kInt8Pv8, kFp16Mask, kInt8Mask };
 
 int launch_fwd(FwdKind kind, int head_dim, bool causal, const FwdParams& p, hipStream_t st);
 

@@ -102,6 +102,27 @@ struct StageV8 {
     static_assert(D * kV8ChunksPerRow % kThreads == 0, "tile split");
 };
 
+// Tile-mask lists: for each query tile, a run of entries e = (key tile << 2)
+// | type in a CSR list (row pointers per query tile); type 1 = every key of
+// the tile visible, 2 = key j visible iff j <= query i, 0 = none visible (3 is
+// read as 1).  Every index below is clamped, so arbitrary list contents never
+// address outside the row-pointer, entry, K, V or scale buffers.
+__host__ __device__ inline int imax(int a, int b) { return a > b ? a : b; }
+struct MaskRow {
+    int base;    // first entry of the query tile
+    int count;   // entries used (0 .. nkblk)
+};
+__host__ __device__ inline MaskRow mask_row(int rp0, int rp1, int nnz, int nkblk) {
+    MaskRow r;
+    r.base = imin(imax(rp0, 0), imax(nnz, 0));
+    r.count = imin(imax(rp1 - r.base, 0), imin(nkblk, imax(nnz, 0) - r.base));
+    return r;
+}
+// entry index of list position pos (positions past the end repeat the last; count >= 1)
+__host__ __device__ inline int mask_entry_index(const MaskRow& r, int pos) { return r.base + imin(pos, r.count - 1); }
+__host__ __device__ inline int mask_entry_tile(int e, int nkblk) { return imin(imax(e >> 2, 0), nkblk - 1); }
+__host__ __device__ inline int mask_entry_type(int e) { return (e & 3) == 3 ? 1 : (e & 3); }
+
 // Score register r of 32-key sub-tile mt (32x32 MFMA accumulator layout)
 // holds key n0 + g*4 + key_offset(mt, r) of a tile at n0 (g = lane / 32).
 __host__ __device__ constexpr int key_offset(int mt, int r) { return mt * 32 + (r >> 2) * 8 + (r & 3); }

@@ -266,6 +266,56 @@ int attn_decode_fp16(const attn_kv_shape* shape, const void* q_f16, const void* 
                      const void* v_f16, void* o_f16, float* lse, const int32_t* kv_head_map,
                      int causal, float sm_scale, void* workspace, void* stream);
 
+/* ---- Tile-level attention masks (APB-style anchor / passing / local) ------
+ * The APB page computes attention with a FlashAttention kernel whose mask has
+ * a changed shape: on one device the keys are an anchor block (the first
+ * tokens), a passing block (keys and values handed over from earlier devices)
+ * and the local context.  These calls run the forward kernels under any mask
+ * given per tile pair: query tile qt (ATTN_MASK_TILE_Q rows) x key tile kt
+ * (ATTN_MASK_TILE_K keys) with a dense host mask of ceil(seq/TILE_Q) x
+ * ceil(seq/TILE_K) bytes, row-major:
+ *   0  no key of the tile is visible to any query of the query tile;
+ *   1  every key of the tile is visible;
+ *   2  key j is visible to query i iff j <= i (causal within the tile pair).
+ * A query row with no visible key gets O = 0 and lse = -inf.  Q and K share
+ * one sequence length; one mask serves every batch entry and head. */
+#define ATTN_MASK_TILE_Q 128
+#define ATTN_MASK_TILE_K 64
+
+/* Mask dimensions for a sequence length (either pointer may be NULL). */
+int attn_block_mask_tiles(int32_t seq, int32_t* q_tiles, int32_t* k_tiles);
+
+/* Host helper: the APB layout as a tile mask.  Keys (and query positions) are
+ * [anchor | passing | local], local = seq - anchor - passing; anchor and
+ * passing are multiples of ATTN_MASK_TILE_Q.  Anchor queries attend causally
+ * within the anchor; local queries attend to the anchor and passing blocks and
+ * causally to the local block (causal over the concatenation); queries at
+ * passing positions attend to nothing (the passing block only lends keys and
+ * values).  mask: host buffer of q_tiles * k_tiles bytes. */
+int attn_block_mask_apb(int32_t seq, int32_t anchor, int32_t passing, uint8_t* mask);
+
+/* Host helper: the dense tile mask as the list the kernels read.  row_ptr
+ * [q_tiles + 1] and cols [q_tiles * k_tiles] are host buffers; cols[e] =
+ * (kt << 2) | type for the visible tiles of each query tile in key order,
+ * row_ptr[qt] .. row_ptr[qt+1] delimiting query tile qt; *nnz = entries
+ * written.  Type-2 tiles wholly below the diagonal become type 1 and those
+ * wholly above it are dropped (same mask).  Mask values above 2: ATTN_EINVAL. */
+int attn_block_mask_csr(int32_t seq, const uint8_t* mask, int32_t* row_ptr, int32_t* cols, int32_t* nnz);
+
+/* The FP16 and the INT8 forward under a tile mask.  mask_row_ptr and
+ * mask_cols are DEVICE copies of attn_block_mask_csr's output (mask_cols may be
+ * NULL when mask_nnz == 0).  The kernels clamp every list index, so a
+ * malformed list gives unspecified results but never an access outside the
+ * buffers.  Other arguments as attn_fwd_fp16 / attn_fwd_int8 (no causal flag:
+ * the mask says it). */
+int attn_fwd_fp16_masked(const attn_shape* shape, const void* q_f16, const void* k_f16, const void* v_f16,
+                         void* o_f16, float* lse, const int32_t* kv_head_map, const int32_t* mask_row_ptr,
+                         const int32_t* mask_cols, int32_t mask_nnz, float sm_scale, void* stream);
+int attn_fwd_int8_masked(const attn_shape* shape, const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                         const float* k_scale, const void* v_f16, void* o_f16, float* lse,
+                         const int32_t* kv_head_map, const int32_t* mask_row_ptr, const int32_t* mask_cols,
+                         int32_t mask_nnz, float sm_scale, void* stream);
+
 /* Static text for a status code. */
 const char* attn_status_string(int status);
 

@@ -179,8 +179,36 @@ static void check_all_paths(int B, int Hq, int S, bool all_heads) {
     }
 }
 
+// Tile-mask lists: for arbitrary (also malformed) row pointers, entry counts
+// and entries, every list index and every key tile stays in bounds.
+static void check_mask_lists() {
+    unsigned x = 12345u;
+    auto rnd = [&](int lo, int hi) {   // inclusive, xorshift
+        x ^= x << 13; x ^= x >> 17; x ^= x << 5;
+        return lo + static_cast<int>(x % static_cast<unsigned>(hi - lo + 1));
+    };
+    for (int it = 0; it < 200000; ++it) {
+        const int nkblk = rnd(1, 5000), nnz = rnd(0, 3000);
+        const int rp0 = rnd(-100, 3100), rp1 = rnd(-100, 3100);
+        const MaskRow r = mask_row(rp0, rp1, nnz, nkblk);
+        REQUIRE(r.count >= 0 && r.count <= nkblk, "count %d", r.count);
+        if (r.count == 0) continue;
+        REQUIRE(r.base >= 0 && r.base + r.count <= nnz, "base %d count %d nnz %d", r.base, r.count, nnz);
+        for (int pos = 0; pos < r.count + 4; ++pos) {
+            const int idx = mask_entry_index(r, pos);
+            REQUIRE(idx >= 0 && idx < nnz, "entry index %d of %d", idx, nnz);
+        }
+        const int e = static_cast<int>(x);   // any 32-bit entry
+        const int kt = mask_entry_tile(e, nkblk);
+        REQUIRE(kt >= 0 && kt < nkblk, "key tile %d of %d", kt, nkblk);
+        const int ty = mask_entry_type(e);
+        REQUIRE(ty >= 0 && ty <= 2, "type %d", ty);
+    }
+}
+
 int main() {
     long shapes = 0;
+    check_mask_lists();
     for (int S = 1; S <= 300; ++S) {
         check_all_paths<64>(1, 3, S, true);
         check_all_paths<128>(2, 2, S, true);
