@@ -12,7 +12,9 @@ Outside the timed steps it also times the FP8 alternative (attn_quantize_qk_fp8
 attn_fwd_int8_pv8) and, with the CPU leg, reports their accuracy against the
 exact oracle on the sampled rows; and the KV-cache decode kernels
 (attn_decode_int8, attn_decode_fp16) on the decode workload (batch 16, one
-query per sequence over an 8192-token cache), as GB/s against HBM.
+query per sequence over an 8192-token cache), as GB/s against HBM; and the
+tile-masked forwards under the APB layout of the same prefill shape (1024
+anchor, 2048 passing, 5120 local tokens), FLOP over the visible pairs.
 
 Printed: ONE JSON line.  `value` is the INT8 (SageAttention-form) path's
 attention throughput, quantisation included: FLOP / (t_quantize_k +
@@ -261,6 +263,8 @@ def run_workload(name, steps, warmup, cpu=False, cpu_seconds=15.0):
         "cpu_baseline": None,
     }
     rec["paths"]["decode"] = run_decode()
+    if name == DEFAULT_WORKLOAD:
+        rec["paths"]["apb_masked"] = run_apb(qd, kd, vd, qz, w)
     if cpu:
         rec["cpu_baseline"], rec["parity_sample"] = cpu_baseline(w, q, k, v, o8, o16, cpu_seconds,
                                                                  extra={"fp8_qk": of8, "int8_pv8": opv8})
@@ -312,6 +316,38 @@ def run_decode(name="decode_gqa", reps=20):
                     "tokens_per_s": round(B * Sq / (ms * 1e-3), 1),
                     "tflops": round(w.flops() / (ms * 1e-3) / 1e12, 2)}
     out["int8_speedup_over_fp16"] = round(res["fp16"] / res["int8"], 3)
+    return out
+
+
+def run_apb(qd, kd, vd, qz, w, anchor=1024, passing=2048, reps=10):
+    """The LLM-prefill shape under the APB tile mask (keys [anchor | passing |
+    local]): the FP16 and INT8 masked forwards; FLOP over the visible pairs."""
+    import torch
+
+    import bit_quantized_exact_amd as A
+
+    S = w.seq
+    csr = A.block_mask_csr(S, A.apb_block_mask(S, anchor, passing))
+    o = torch.empty_like(qd)
+    stream = torch.cuda.current_stream()
+    res = {}
+    for tag, fn in (("fp16", lambda: A.fwd_fp16_masked(qd, kd, vd, csr, out=o)),
+                    ("int8", lambda: A.fwd_int8_masked(qz, vd, csr, out=o))):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[tag] = e0.elapsed_time(e1) / reps
+    rows = np.r_[0:anchor, anchor + passing:S]
+    pairs = float((rows + 1).sum())
+    flop = 4.0 * w.batch * w.heads_q * w.head_dim * pairs
+    out = {"anchor": anchor, "passing": passing, "local": S - anchor - passing, "mask_tiles_listed": csr["nnz"]}
+    for tag in ("fp16", "int8"):
+        out[tag] = {"ms": round(res[tag], 4), "tflops": round(flop / (res[tag] * 1e-3) / 1e12, 2)}
     return out
 
 

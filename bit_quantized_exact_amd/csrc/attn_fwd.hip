@@ -202,8 +202,9 @@ void fwd_kernel(const FwdParams p) {
     const int S = p.S;
 
     // ---- block id -> (batch, q-head, query tile), XCD-aware ----
+    // (tile masks are mostly causal-like too, heavier for later query tiles)
     const geom::BlockCoord bc = geom::decode_block(blockIdx.x, gridDim.x, p.Hq, p.ntiles, p.tile_lo,
-                                                   CAUSAL && !DUMP);
+                                                   (CAUSAL || BMASK) && !DUMP);
     const int b = bc.b;
     const int h = p.horder[bc.pos];
     const int kvh = p.kvmap[h];
