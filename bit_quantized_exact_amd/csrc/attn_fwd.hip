@@ -90,6 +90,8 @@ struct Cfg : geom::Stage<D, INT8> {
     static constexpr int VPT = PV8 ? geom::StageV8<D>::VPT : G::VPT;
     static constexpr int KBYTES = kBN * KROW;
     static constexpr int VBYTES = (PV8 ? D : kBN) * VROW;
+    static constexpr int KSTAGE = kBN * KROWG;                 // unpadded tiles (direct-to-LDS staging)
+    static constexpr int VSTAGE = kBN * 2 * D;
     static constexpr int DT = D / 32;                          // 32-row d tiles of O^T
     static_assert(kBN * KCPR % kFwdThreads == 0 && kBN * VCPR % kFwdThreads == 0, "tile split");
     static_assert(geom::kTileM == kBM && geom::kTileN == kBN && geom::kThreads == kFwdThreads, "geometry");
@@ -128,6 +130,25 @@ __device__ __forceinline__ float row_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Direct-to-LDS staging synchronisation: wait until at most VM vector-memory
+// operations of this wave are outstanding (its earlier tile copies have
+// landed in LDS) and its own LDS reads are done, then a workgroup barrier.
+// A bare s_barrier, because __syncthreads also waits for every outstanding
+// copy, which would drain the prefetch; the empty asm statements keep the
+// compiler from moving memory operations across the wait and the barrier.
+template <int VM>
+__device__ __forceinline__ void lds_stage_barrier() {
+    static_assert(VM >= 0 && VM < 64, "vmcnt range");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((VM & 0xF) | (0x7 << 4) | (0x0 << 8) | ((VM >> 4) << 14));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+#ifndef ATTN_FWD_DTL
+#define ATTN_FWD_DTL 1
+#endif
+
 // Transposed scores of one 64-key tile for this wave's 32 queries:
 // acc[mt] holds keys mt*32 + (r/4)*8 + (lane/32)*4 + r%4 (register r) of query
 // lane%32.  The same code feeds the forward and the INT32 score dump.
@@ -135,10 +156,16 @@ __device__ __forceinline__ float row_sum(float x) {
 // v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3, fp32 accumulation); A and B take
 // their bytes from the same k positions, so the products pair up as in the
 // INT8 form.
-template <int D, bool INT8, bool F8 = false, bool BIASED = false>
+template <int D, bool INT8, bool F8 = false, bool BIASED = false, bool SWZ = false>
 __device__ __forceinline__ void score_tile(const char* ks, const typename Cfg<D, INT8, F8>::qfrag_t* qf,
                                            int l32, int g, typename Cfg<D, INT8, F8>::acc_t acc[2]) {
     using C = Cfg<D, INT8, F8>;
+    // 16-byte chunk `chunk` of K row `row`: padded rows, or the swizzled
+    // unpadded rows of direct-to-LDS staging
+    auto kchunk = [&](int row, int chunk) -> const char* {
+        if constexpr (SWZ) return ks + row * C::KROWG + ((chunk ^ geom::Dtl<C::KROWG>::k_swz(row)) << 4);
+        else return ks + row * C::KROW + (chunk << 4);
+    };
     static_assert(!BIASED || (INT8 && !F8), "the bias applies to INT32 accumulators");
     if constexpr (BIASED) {
         acc[0] = kI8BiasBits;
@@ -153,9 +180,8 @@ __device__ __forceinline__ void score_tile(const char* ks, const typename Cfg<D,
             const i8x b = __builtin_shufflevector(qf[2 * s2], qf[2 * s2 + 1], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
-                const char* row = ks + (mt * 32 + l32) * C::KROW + g * 16;
-                const i4x a0 = *reinterpret_cast<const i4x*>(row + (2 * s2) * 32);
-                const i4x a1 = *reinterpret_cast<const i4x*>(row + (2 * s2 + 1) * 32);
+                const i4x a0 = *reinterpret_cast<const i4x*>(kchunk(mt * 32 + l32, 2 * (2 * s2) + g));
+                const i4x a1 = *reinterpret_cast<const i4x*>(kchunk(mt * 32 + l32, 2 * (2 * s2 + 1) + g));
                 const i8x a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
                 acc[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[mt], 0, 0, 0, 0, 0, 0);
             }
@@ -167,10 +193,10 @@ __device__ __forceinline__ void score_tile(const char* ks, const typename Cfg<D,
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
             if constexpr (INT8) {
-                const i4x a = *reinterpret_cast<const i4x*>(ks + (mt * 32 + l32) * C::KROW + s * 32 + g * 16);
+                const i4x a = *reinterpret_cast<const i4x*>(kchunk(mt * 32 + l32, 2 * s + g));
                 acc[mt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[s], acc[mt], 0, 0, 0);
             } else {
-                const h8 a = *reinterpret_cast<const h8*>(ks + (mt * 32 + l32) * C::KROW + (s * 16 + g * 8) * 2);
+                const h8 a = *reinterpret_cast<const h8*>(kchunk(mt * 32 + l32, 2 * s + g));
                 acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[s], acc[mt], 0, 0, 0);
             }
         }
@@ -190,7 +216,20 @@ void fwd_kernel(const FwdParams p) {
     using C = Cfg<D, INT8, F8, PV8>;
     typedef typename C::qfrag_t qfrag_t;
     typedef typename C::acc_t acc_t;
-    __shared__ __attribute__((aligned(16))) char smem[2 * C::KBYTES + (DUMP ? 0 : 2 * C::VBYTES)];
+    // Staging: direct-to-LDS copies into unpadded swizzled stages (NST of
+    // them, one array each so that the compiler can tell the copies of
+    // different stages apart), or the register path into padded tiles (the
+    // score dump and the 8-bit V^T tiles).
+    // (the tile-masked variant reads its key-tile list per iteration with
+    // wave-uniform loads, which copies into LDS would turn into vector loads
+    // that drain the copy queue; it keeps the register path)
+    constexpr bool DTL = ATTN_FWD_DTL && !DUMP && !PV8 && !BMASK;
+    constexpr int NST = (!INT8 && D == 128) ? 2 : 3;
+    __shared__ __attribute__((aligned(16))) char smem[DTL ? 16 : 2 * C::KBYTES + (DUMP ? 0 : 2 * C::VBYTES)];
+    __shared__ __attribute__((aligned(16))) char dk0[DTL ? C::KSTAGE : 16], dk1[DTL ? C::KSTAGE : 16],
+        dk2[DTL && NST == 3 ? C::KSTAGE : 16];
+    __shared__ __attribute__((aligned(16))) char dv0[DTL ? C::VSTAGE : 16], dv1[DTL ? C::VSTAGE : 16],
+        dv2[DTL && NST == 3 ? C::VSTAGE : 16];
     auto kbuf = [&](int i) { return smem + i * C::KBYTES; };
     auto vbuf = [&](int i) { return smem + 2 * C::KBYTES + i * C::VBYTES; };
 
@@ -326,9 +365,64 @@ void fwd_kernel(const FwdParams p) {
         }
     };
 
+    // direct-to-LDS copies of one tile into a stage: instruction i of this
+    // wave fills bytes (wave*NI + i)*1024 .. +1023 of the stage; each lane
+    // fetches the logical chunk its slot holds (row clamped to the sequence)
+    using DK = geom::Dtl<C::KROWG>;
+    using DV = geom::Dtl<2 * D>;
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    auto dtl_k = [&](int n0, char* st) __attribute__((always_inline)) {
+        const int first = geom::tile_first_row(n0, S);
+        const char* base = kg + static_cast<size_t>(first) * C::KROWG;
+#pragma unroll
+        for (int i = 0; i < DK::NI; ++i) {
+            const int r = DK::slot_row(wave, i, lane);
+            const int c = DK::slot_chunk(wave, i, lane) ^ DK::k_swz(r);
+            const uint32_t off = static_cast<uint32_t>(geom::tile_lane_row(r, first, S)) * C::KROWG + c * 16;
+            __builtin_amdgcn_global_load_lds(base + off,
+                                             (__attribute__((address_space(3))) void*)(st + (wave_s * DK::NI + i) * 1024),
+                                             16, 0, 0);
+        }
+    };
+    auto dtl_v = [&](int n0, char* st) __attribute__((always_inline)) {
+        const int first = geom::tile_first_row(n0, S);
+        const char* base = vg + static_cast<size_t>(first) * C::VROWG;
+#pragma unroll
+        for (int i = 0; i < DV::NI; ++i) {
+            const int r = DV::slot_row(wave, i, lane);
+            const int c = DV::slot_chunk(wave, i, lane) ^ DV::v_swz(r);
+            const uint32_t off = static_cast<uint32_t>(geom::tile_lane_row(r, first, S)) * C::VROWG + c * 16;
+            __builtin_amdgcn_global_load_lds(base + off,
+                                             (__attribute__((address_space(3))) void*)(st + (wave_s * DV::NI + i) * 1024),
+                                             16, 0, 0);
+        }
+    };
+    char* dks[3] = {dk0, dk1, dk2};
+    char* dvs[3] = {dv0, dv1, dv2};
+    // K scale of key tile t (clamped to the last block; tiles past the end are never used)
+    auto kscale_at = [&](int t) -> float {
+        return p.k_scale[bhk * p.nkblk + geom::imin(t, p.nkblk - 1)];
+    };
+    float ksring[3] = {1.0f, 1.0f, 1.0f};
+
     // The first K tile's loads are issued before Q is read and quantised,
-    // so the two latencies overlap.
-    if constexpr (!DUMP) gload_k(tile_row(0), kreg[0]);
+    // so the two latencies overlap (direct-to-LDS: the whole prologue's
+    // copies, K_0 .. K_{NST-1} and V_0 .. V_{NST-2}).
+    if constexpr (DTL) {
+        dtl_k(tile_row(0), dks[0]);
+        dtl_k(tile_row(1), dks[1]);
+        dtl_v(tile_row(0), dvs[0]);
+        if constexpr (NST == 3) {
+            dtl_k(tile_row(2), dks[2]);
+            dtl_v(tile_row(1), dvs[1]);
+        }
+        if constexpr (INT8) {
+#pragma unroll
+            for (int t = 0; t < NST; ++t) ksring[t] = kscale_at(t);
+        }
+    } else if constexpr (!DUMP) {
+        gload_k(tile_row(0), kreg[0]);
+    }
 
     // ---- Q fragment (B operand of S^T = K Q^T), kept in VGPRs.  Rows past
     // the sequence read the last row; they are never stored.
@@ -433,18 +527,23 @@ void fwd_kernel(const FwdParams p) {
         // depth 2, K_2 and V_1 into the second register set) ----
         constexpr bool kBiased = INT8 && !F8;   // INT32 scores read as biased fp32
         acc_t sc[2];
-        sstore_k(0, kreg[0]);
-        __syncthreads();
-        score_tile<D, INT8, F8, kBiased>(kbuf(0), qf, l32, g, sc);
-        gload_k(tile_row(1), kreg[0]);
-        gload_v(tile_row(0), vreg[0]);
-        sstore_k(1, kreg[0]);
-        sstore_v(0, vreg[0]);
-        if constexpr (DEPTH == 2) {
-            gload_k(tile_row(2), kreg[DEPTH - 1]);
-            gload_v(tile_row(1), vreg[DEPTH - 1]);
+        if constexpr (DTL) {
+            lds_stage_barrier<0>();   // every prologue copy has landed
+            score_tile<D, INT8, F8, kBiased, true>(dks[0], qf, l32, g, sc);
+        } else {
+            sstore_k(0, kreg[0]);
+            __syncthreads();
+            score_tile<D, INT8, F8, kBiased>(kbuf(0), qf, l32, g, sc);
+            gload_k(tile_row(1), kreg[0]);
+            gload_v(tile_row(0), vreg[0]);
+            sstore_k(1, kreg[0]);
+            sstore_v(0, vreg[0]);
+            if constexpr (DEPTH == 2) {
+                gload_k(tile_row(2), kreg[DEPTH - 1]);
+                gload_v(tile_row(1), vreg[DEPTH - 1]);
+            }
+            __syncthreads();
         }
-        __syncthreads();
 
         // ---- main loop: at entry sc holds S_j; LDS holds K_{j+1} and V_j.
         // Loads and stores run unconditionally (tiles past the end read the
@@ -452,16 +551,17 @@ void fwd_kernel(const FwdParams p) {
         // make the compiler wait for every outstanding load at the loop head.
         // Iteration j loads into set LS and writes set SS to LDS (the same set
         // at depth 1; the set loaded one iteration earlier at depth 2).
-        auto step = [&](int j, auto ls_tag) {
-            constexpr int LS = decltype(ls_tag)::value;
-            constexpr int SS = DEPTH == 2 ? 1 - LS : LS;
+        // One key tile: the softmax of S_j, the scores S_{j+1} from the K tile
+        // at ksn and O^T += V_j^T P_j^T from the V tile at vsc (padded rows,
+        // or the swizzled unpadded rows of direct-to-LDS staging when SWZ).
+        auto compute = [&](int j, const char* ksn, const char* vsc, float kscale_j, auto swz_tag)
+                           __attribute__((always_inline)) {
+            constexpr bool SWZ = decltype(swz_tag)::value;
             const int n0 = tile_row(j);
-            gload_k(BMASK ? tile_row(j + 1 + DEPTH) : geom::k_load_row<DEPTH>(j), kreg[LS]);
-            gload_v(BMASK ? tile_row(j + DEPTH) : geom::v_load_row<DEPTH>(j), vreg[LS]);
-            if (j < nkt_w) {
+            {
                 // scores in log2 units: s * c with c = (dQ dK) sm_scale log2(e)
                 float c = p.scale_log2;
-                if constexpr (INT8) c = fmaxf(qscale * kscale[bhk * p.nkblk + (BMASK ? n0 / kBN : j)] * p.scale_log2, FLT_MIN);
+                if constexpr (INT8) c = fmaxf(qscale * kscale_j * p.scale_log2, FLT_MIN);
                 float sv[2][16];
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt)
@@ -505,7 +605,7 @@ void fwd_kernel(const FwdParams p) {
 
                 // scores of the next tile (MFMA) overlap the exponentials (VALU)
                 acc_t sn[2];
-                score_tile<D, INT8, F8, kBiased>(kbuf((j + 1) & 1), qf, l32, g, sn);
+                score_tile<D, INT8, F8, kBiased, SWZ>(ksn, qf, l32, g, sn);
 
                 const float m_eff = BMASK && m_run == -INFINITY ? 0.0f : m_run;   // (masked rows: weights 0)
                 const float negm = kBiased ? -__builtin_fmaf(kI8Bias, c, m_eff) : -m_eff;
@@ -532,7 +632,7 @@ void fwd_kernel(const FwdParams p) {
                         w = __builtin_amdgcn_cvt_pk_fp8_f32(q[2] * 448.0f, q[3] * 448.0f, w, true);
                         pb8[k] = w;
                     }
-                    const char* vs = vbuf(j & 1);
+                    const char* vs = vsc;
 #pragma unroll
                     for (int dt = 0; dt < C::DT; ++dt) {
                         const char* row = vs + (dt * 32 + l32) * C::VROW + g * 32;
@@ -552,16 +652,21 @@ void fwd_kernel(const FwdParams p) {
                 }
 
                 // ---- O^T += V^T P^T ----
-                const char* vs = vbuf(j & 1);
+                const char* vs = vsc;
                 const int grp = lane >> 4, li = lane & 15;
+                // byte b of V row `row` (padded rows, or swizzled 16-byte chunks)
+                auto vbyte = [&](int row, int b) -> const char* {
+                    if constexpr (SWZ) return vs + row * (2 * D) + (((b >> 4) ^ DV::v_swz(row)) << 4) + (b & 15);
+                    else return vs + row * C::VROW + b;
+                };
 #pragma unroll
                 for (int dt = 0; dt < C::DT; ++dt) {
-                    const char* vb = vs + (dt * 32 + (grp & 1) * 16 + (li & 3) * 4) * 2;
+                    const int vb = (dt * 32 + (grp & 1) * 16 + (li & 3) * 4) * 2;
 #pragma unroll
                     for (int k4 = 0; k4 < 4; ++k4) {
                         const int krow = k4 * 16 + g * 4 + (li >> 2);
-                        const tr4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_tr4*)(vb + krow * C::VROW));
-                        const tr4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_tr4*)(vb + (krow + 8) * C::VROW));
+                        const tr4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_tr4*)vbyte(krow, vb));
+                        const tr4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_tr4*)vbyte(krow + 8, vb));
                         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(join(lo, hi), pb[k4], oacc[dt], 0, 0, 0);
                     }
                 }
@@ -577,11 +682,50 @@ void fwd_kernel(const FwdParams p) {
                 sc[1] = sn[1];
                 }
             }
+        };
+        // register staging: iteration j loads into set LS and writes set SS
+        // to LDS (the same set at depth 1; the set loaded one iteration earlier
+        // at depth 2)
+        auto step = [&](int j, auto ls_tag) __attribute__((always_inline)) {
+            constexpr int LS = decltype(ls_tag)::value;
+            constexpr int SS = DEPTH == 2 ? 1 - LS : LS;
+            gload_k(BMASK ? tile_row(j + 1 + DEPTH) : geom::k_load_row<DEPTH>(j), kreg[LS]);
+            gload_v(BMASK ? tile_row(j + DEPTH) : geom::v_load_row<DEPTH>(j), vreg[LS]);
+            if (j < nkt_w) {
+                float ksj = 1.0f;
+                if constexpr (INT8) ksj = kscale[bhk * p.nkblk + (BMASK ? tile_row(j) / kBN : j)];
+                compute(j, kbuf((j + 1) & 1), vbuf(j & 1), ksj, std::false_type{});
+            }
             sstore_k(j & 1, kreg[SS]);
             sstore_v((j + 1) & 1, vreg[SS]);
             __syncthreads();
         };
-        if constexpr (DEPTH == 2) {
+        // direct-to-LDS staging, iteration j (J = j mod NST): K_{j+1} and V_j
+        // must have landed (the copies of the last iteration may stay in
+        // flight at NST = 3), then after the barrier K_{j+NST} goes into the
+        // stage K_j left and V_{j+NST-1} into the stage V_{j-1} left.
+        // The K scale of tile j is loaded with tile j's copies (NST iterations
+        // earlier) into slot J of a small register ring: a wave-uniform load
+        // becomes a vector load once copies into LDS are in flight, and loaded
+        // late it would make the compiler wait for the whole copy queue.
+        auto dstep = [&](int j, auto j_tag) __attribute__((always_inline)) {
+            constexpr int J = decltype(j_tag)::value;
+            const float ksj = ksring[J];
+            lds_stage_barrier<NST == 3 ? DK::NI + DV::NI + (INT8 ? 1 : 0) : 0>();
+            dtl_k(tile_row(j + NST), dks[J]);
+            if constexpr (INT8) ksring[J] = kscale_at(j + NST);
+            dtl_v(tile_row(j + NST - 1), dvs[(J + NST - 1) % NST]);
+            if (j < nkt_w) compute(j, dks[(J + 1) % NST], dvs[J], ksj, std::true_type{});
+        };
+        if constexpr (DTL) {
+            const int iters = geom::dtl_loop_iterations<NST>(nkt);
+            for (int j = 0; j < iters; j += NST) {
+                dstep(j, std::integral_constant<int, 0>{});
+                dstep(j + 1, std::integral_constant<int, 1>{});
+                if constexpr (NST == 3) dstep(j + 2, std::integral_constant<int, 2>{});
+            }
+            lds_stage_barrier<0>();   // no copy may still be landing when the workgroup ends
+        } else if constexpr (DEPTH == 2) {
             const int iters = geom::loop_iterations<2>(nkt);
             for (int j = 0; j < iters; j += 2) {
                 step(j, std::integral_constant<int, 0>{});

@@ -89,6 +89,27 @@ struct Stage {
     }
 };
 
+// Direct-to-LDS staging (global_load_lds): one wave instruction moves 64
+// lanes x 16 bytes into 1 KB of LDS at a wave-uniform base, lane l writing
+// bytes 16 l .. 16 l + 15.  A 64-row tile of RB-byte rows takes 64*RB/1024
+// wave instructions, NI per wave (wave w issues w*NI .. w*NI+NI-1).  Rows are
+// stored unpadded; the 16-byte chunks of each row are permuted by an XOR with
+// a row-dependent value so that the MFMA operand reads of K (16 rows, one
+// chunk) and the transposing reads of V (4 rows, 64 bytes) hit 64 distinct
+// banks.  Slot (w, i, lane) holds physical chunk pc of row r, i.e. logical
+// chunk pc ^ swz(r) of key row r (the XOR is its own inverse).
+template <int RB>
+struct Dtl {
+    static constexpr int CPR = RB / 16;                   // chunks per row
+    static constexpr int RPL = RB >= 256 ? 1 : 256 / RB;  // rows per 256-byte bank line
+    static constexpr int NI = kTileN * RB / 1024 / 4;     // instructions per wave per tile
+    static_assert(kTileN * RB % 4096 == 0 && CPR >= 4, "tile split");
+    __host__ __device__ static constexpr int k_swz(int r) { return (r / RPL) % CPR; }
+    __host__ __device__ static constexpr int v_swz(int r) { return ((r / RPL) % (4 / RPL)) * 4; }
+    __host__ __device__ static constexpr int slot_row(int w, int i, int lane) { return ((w * NI + i) * 64 + lane) / CPR; }
+    __host__ __device__ static constexpr int slot_chunk(int w, int i, int lane) { return ((w * NI + i) * 64 + lane) % CPR; }
+};
+
 // 8-bit V of the P.V ablation: V^T codes [B*Hkv, D, Sp], Sp = 64 * nkblk.
 // A key tile at n0 is D rows of 64 bytes starting at column
 // v8_tile_col(n0, nkblk); tiles prefetched past the end are clamped to the
@@ -153,6 +174,12 @@ template <int DEPTH>
 __host__ __device__ inline int v_load_row(int j) { return (j + DEPTH) * kTileN; }
 template <int DEPTH>
 __host__ __device__ inline int loop_iterations(int nkt) { return DEPTH == 2 ? (nkt + 1) & ~1 : nkt; }
+// Direct-to-LDS staging with NST stages: the prologue copies K tiles
+// 0..NST-1 and V tiles 0..NST-2; iteration j copies K tile j+NST and V tile
+// j+NST-1 (tiles past the end copy clamped rows); the loop runs a multiple
+// of NST iterations.
+template <int NST>
+__host__ __device__ inline int dtl_loop_iterations(int nkt) { return (nkt + NST - 1) / NST * NST; }
 
 }  // namespace geom
 }  // namespace attn

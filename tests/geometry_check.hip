@@ -114,6 +114,53 @@ static void check_shape(int B, int Hq, int S, bool causal, bool dump, int tile_l
                 vn0.push_back(depth == 2 ? v_load_row<2>(j) : v_load_row<1>(j));
             }
         }
+        // direct-to-LDS staging (all non-dump variants except the 8-bit V^T
+        // one): every (wave, instruction, lane) slot of every copied tile
+        if (!dump && !pv8) {
+            const int nst = (!INT8 && D == 128) ? 2 : 3;
+            std::vector<int> dk, dvv;
+            for (int t = 0; t < nst; ++t) dk.push_back(t * kTileN);
+            for (int t = 0; t + 1 < nst; ++t) dvv.push_back(t * kTileN);
+            const int iters = nst == 2 ? dtl_loop_iterations<2>(nkt) : dtl_loop_iterations<3>(nkt);
+            REQUIRE(iters >= nkt && iters % nst == 0, "dtl iterations %d", iters);
+            for (int j = 0; j < iters; ++j) {
+                dk.push_back((j + nst) * kTileN);
+                dvv.push_back((j + nst - 1) * kTileN);
+                const int ks = j + nst < nkblk ? j + nst : nkblk - 1;   // scale ring index, clamped
+                REQUIRE(ks >= 0 && ks < nkblk, "k scale ring %d", ks);
+            }
+            auto check_tile = [&](int n0, int rb, size_t head_bytes, bool is_v) {
+                const int first = tile_first_row(n0, S);
+                const int cpr = rb / 16, ni = kTileN * rb / 1024 / 4;
+                std::vector<int> seen_slot(static_cast<size_t>(kTileN) * cpr, 0);
+                for (int w = 0; w < 4; ++w)
+                    for (int i = 0; i < ni; ++i)
+                        for (int lane = 0; lane < 64; ++lane) {
+                            int r, pc, c;
+                            if (rb == 256) {
+                                r = Dtl<256>::slot_row(w, i, lane); pc = Dtl<256>::slot_chunk(w, i, lane);
+                                c = pc ^ (is_v ? Dtl<256>::v_swz(r) : Dtl<256>::k_swz(r));
+                            } else if (rb == 128) {
+                                r = Dtl<128>::slot_row(w, i, lane); pc = Dtl<128>::slot_chunk(w, i, lane);
+                                c = pc ^ (is_v ? Dtl<128>::v_swz(r) : Dtl<128>::k_swz(r));
+                            } else {
+                                r = Dtl<64>::slot_row(w, i, lane); pc = Dtl<64>::slot_chunk(w, i, lane);
+                                c = pc ^ Dtl<64>::k_swz(r);
+                            }
+                            REQUIRE(r >= 0 && r < kTileN && pc >= 0 && pc < cpr && c >= 0 && c < cpr,
+                                    "dtl slot r %d pc %d c %d", r, pc, c);
+                            // the LDS byte the lane writes is the slot's own position
+                            REQUIRE((w * ni + i) * 1024 + lane * 16 == r * rb + pc * 16, "dtl lds byte");
+                            seen_slot[static_cast<size_t>(r) * cpr + pc] += 1;
+                            const int row = tile_lane_row(r, first, S);
+                            const size_t off = (static_cast<size_t>(first) + row) * rb + c * 16;
+                            REQUIRE(first + row <= S - 1 && off + 16 <= head_bytes, "dtl byte %zu of %zu", off, head_bytes);
+                        }
+                for (int v : seen_slot) REQUIRE(v == 1, "dtl slot written %d times", v);
+            };
+            for (int n0 : dk) check_tile(n0, St::KROWG, qk_head_bytes, false);
+            for (int n0 : dvv) check_tile(n0, St::VROWG, v_head_bytes, true);
+        }
         for (int n0 : kn0) {
             const int first = tile_first_row(n0, S);
             REQUIRE(first >= 0 && first <= S - 1, "k first row %d (n0 %d, S %d)", first, n0, S);
