@@ -224,7 +224,10 @@ void fwd_kernel(const FwdParams p) {
     // wave-uniform loads, which copies into LDS would turn into vector loads
     // that drain the copy queue; it keeps the register path)
     constexpr bool DTL = ATTN_FWD_DTL && !DUMP && !PV8 && !BMASK;
-    constexpr int NST = (!INT8 && D == 128) ? 2 : 3;
+#ifndef ATTN_FWD_NST_F16_D128
+#define ATTN_FWD_NST_F16_D128 2
+#endif
+    constexpr int NST = (!INT8 && D == 128) ? ATTN_FWD_NST_F16_D128 : 3;
     __shared__ __attribute__((aligned(16))) char smem[DTL ? 16 : 2 * C::KBYTES + (DUMP ? 0 : 2 * C::VBYTES)];
     __shared__ __attribute__((aligned(16))) char dk0[DTL ? C::KSTAGE : 16], dk1[DTL ? C::KSTAGE : 16],
         dk2[DTL && NST == 3 ? C::KSTAGE : 16];
