@@ -80,8 +80,11 @@ def counters_for(kernel_tag: str, workload: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    src = os.path.join(ROOT, "bit_quantized_exact_amd", "csrc", vals.get("source", "attn_fwd.hip"))
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    # the kernel is its source file plus the headers it includes, hashed in the listed order
+    h = hashlib.sha256()
+    for name in vals.get("source", "attn_fwd.hip").split():
+        h.update(open(os.path.join(ROOT, "bit_quantized_exact_amd", "csrc", name), "rb").read())
+    sha = h.hexdigest()
     if vals.get("source_sha256") != sha:
         return None
     try:
