@@ -10,9 +10,10 @@
 //
 // Every result here is bit-exact by construction and independent of launch
 // order and reduction order:
-//   * the channel sum is accumulated exactly in int64 fixed point (every fp16
-//     value is an integer multiple of 2^-24, below 2^40 in those units), so
-//     any summation order gives the same integer;
+//   * the channel sum is exact (every fp16 value is an integer multiple of
+//     2^-24, below 2^40 in those units): fp64 within a chunk of tokens, then
+//     int64 in those units across chunks, so any summation order gives the
+//     same integer (finite inputs);
 //   * maxima are exact;
 //   * the remaining fp32 operations (subtract, two correctly rounded
 //     divisions, one product, rint) are single IEEE operations.  This file is
@@ -30,14 +31,6 @@ namespace {
 typedef int i4x __attribute__((ext_vector_type(4)));
 typedef int i2x __attribute__((ext_vector_type(2)));
 
-// fp16 bit pattern -> exact value in units of 2^-24 (finite inputs).
-__device__ __forceinline__ long long half_to_fixed(unsigned h) {
-    const int e = (h >> 10) & 31;
-    const int f = h & 1023;
-    const long long mag = e ? (static_cast<long long>(1024 + f) << (e - 1)) : f;
-    return (h & 0x8000u) ? -mag : mag;
-}
-
 __device__ __forceinline__ float half_bits_to_float(unsigned h) {
     _Float16 x;
     const unsigned short s = static_cast<unsigned short>(h);
@@ -46,56 +39,91 @@ __device__ __forceinline__ float half_bits_to_float(unsigned h) {
 }
 
 // Per (b, kv-head, chunk of kSumChunk tokens): exact column sums of K.
-// Thread t owns one 16-byte column chunk (8 channels) and a strided set of
-// rows; the row groups are then combined through LDS (integer adds).
+// Thread t owns one 16-byte column chunk (8 channels) and every RG-th row of
+// the chunk; all of its row loads are issued before the first add (rows past
+// the sequence read the last row and are dropped).  The sums are taken in
+// fp64, which is exact here: every fp16 value is an integer multiple of 2^-24
+// below 2^40 in those units, so any sum of at most kSumChunk of them is such
+// a multiple below 2^48 < 2^53.  The chunk total is then stored as that
+// integer (int64), which keeps the cross-chunk total exact in any order.
+constexpr int kColsumThreads = 512;
 template <int D>
-__global__ __launch_bounds__(256) void k_colsum_kernel(const uint16_t* __restrict__ k, int S,
-                                                       int nchunk,
-                                                       long long* __restrict__ partial) {
-    constexpr int CPR = D / 8;          // 16-byte chunks per row
-    constexpr int RG = 256 / CPR;       // row groups
-    __shared__ long long red[RG][D];
+__global__ __launch_bounds__(kColsumThreads) void k_colsum_kernel(const uint16_t* __restrict__ k, int S,
+                                                                  int nchunk,
+                                                                  long long* __restrict__ partial) {
+    constexpr int CPR = D / 8;                  // 16-byte chunks per row
+    constexpr int RG = kColsumThreads / CPR;    // row groups
+    constexpr int RPT = kSumChunk / RG;         // rows per thread
+    static_assert(kSumChunk % RG == 0 && kSumChunk * 65536.0 * 16777216.0 < 9007199254740992.0,
+                  "exact fp64 chunk sums");
+    __shared__ double red[RG][D];
     const int t = threadIdx.x;
     const int cc = t % CPR, rg = t / CPR;
     const int chunk = blockIdx.x;
     const size_t bk = blockIdx.y;
-    const uint16_t* base = k + bk * static_cast<size_t>(S) * D;
-    long long acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    const int r0 = chunk * kSumChunk;
-    for (int r = r0 + rg; r < r0 + kSumChunk && r < S; r += RG) {
-        const i4x v = *reinterpret_cast<const i4x*>(base + static_cast<size_t>(r) * D + cc * 8);
+    const uint16_t* base = k + bk * static_cast<size_t>(S) * D + cc * 8;
+    const int r0 = chunk * kSumChunk + rg;
+    i4x v[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int r = r0 + i * RG;
+        v[i] = *reinterpret_cast<const i4x*>(base + static_cast<size_t>(r < S ? r : S - 1) * D);
+    }
+    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        if (r0 + i * RG >= S) break;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const unsigned w = static_cast<unsigned>(v[e]);
-            acc[2 * e] += half_to_fixed(w & 0xffffu);
-            acc[2 * e + 1] += half_to_fixed(w >> 16);
+            const unsigned w = static_cast<unsigned>(v[i][e]);
+            acc[2 * e] += static_cast<double>(half_bits_to_float(w & 0xffffu));
+            acc[2 * e + 1] += static_cast<double>(half_bits_to_float(w >> 16));
         }
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) red[rg][cc * 8 + e] = acc[e];
     __syncthreads();
     if (t < D) {
-        long long s = 0;
+        double s = 0.0;
+#pragma unroll
         for (int g = 0; g < RG; ++g) s += red[g][t];
-        partial[(bk * nchunk + chunk) * D + t] = s;
+        partial[(bk * nchunk + chunk) * D + t] = static_cast<long long>(__builtin_ldexp(s, 24));
     }
 }
 
-// Per (b, kv-head): total over chunks, mu = fp32(fp64(sum) / S).
+// Per (b, kv-head): total over chunks, mu = fp32(fp64(sum) / S).  kMeanGroups
+// threads per channel each add every kMeanGroups-th chunk (loads unrolled so
+// they are in flight together), then LDS combines the groups.
+constexpr int kMeanGroups = 4;
 template <int D>
-__global__ __launch_bounds__(D) void k_mean_kernel(const long long* __restrict__ partial, int S,
-                                                   int nchunk, float* __restrict__ mean,
-                                                   float* __restrict__ mean_out) {
+__global__ __launch_bounds__(D * kMeanGroups) void k_mean_kernel(const long long* __restrict__ partial, int S,
+                                                                 int nchunk, float* __restrict__ mean,
+                                                                 float* __restrict__ mean_out) {
+    __shared__ long long red[kMeanGroups][D];
     const size_t bk = blockIdx.x;
-    const int c = threadIdx.x;
-    long long s = 0;
-    for (int i = 0; i < nchunk; ++i) s += partial[(bk * nchunk + i) * D + c];
-    // (double)s is exact below 2^53 and correctly rounded above; the 2^-24
-    // scaling is exact; the division and the narrowing are IEEE operations.
-    const double total = __builtin_ldexp(static_cast<double>(s), -24);
-    const float mu = static_cast<float>(total / static_cast<double>(S));
-    mean[bk * D + c] = mu;
-    if (mean_out) mean_out[bk * D + c] = mu;
+    const int c = threadIdx.x % D, grp = threadIdx.x / D;
+    const long long* src = partial + bk * static_cast<size_t>(nchunk) * D + c;
+    long long s[4] = {0, 0, 0, 0};
+    int i = grp;
+    for (; i + 3 * kMeanGroups < nchunk; i += 4 * kMeanGroups) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) s[u] += src[static_cast<size_t>(i + u * kMeanGroups) * D];
+    }
+    for (; i < nchunk; i += kMeanGroups) s[0] += src[static_cast<size_t>(i) * D];
+    red[grp][c] = (s[0] + s[1]) + (s[2] + s[3]);
+    __syncthreads();
+    if (grp == 0) {
+        long long tot = 0;
+#pragma unroll
+        for (int g = 0; g < kMeanGroups; ++g) tot += red[g][c];
+        // (double)tot is exact below 2^53 and correctly rounded above; the
+        // 2^-24 scaling is exact; the division and the narrowing are IEEE
+        // operations.
+        const double total = __builtin_ldexp(static_cast<double>(tot), -24);
+        const float mu = static_cast<float>(total / static_cast<double>(S));
+        mean[bk * D + c] = mu;
+        if (mean_out) mean_out[bk * D + c] = mu;
+    }
 }
 
 __device__ __forceinline__ float block_max(float v, float* red) {
@@ -213,18 +241,26 @@ __global__ __launch_bounds__(256) void v_colmax_kernel(const uint16_t* __restric
     const int cc = t % CPR, rg = t / CPR;
     const int chunk = blockIdx.x;
     const size_t bk = blockIdx.y;
-    const uint16_t* base = v + bk * static_cast<size_t>(S) * D;
+    constexpr int RPT = kSumChunk / RG;
+    const uint16_t* base = v + bk * static_cast<size_t>(S) * D + cc * 8;
+    const int r0 = chunk * kSumChunk + rg;
+    // every row load in flight before the first max (rows past the sequence
+    // read the last row, which leaves the maxima unchanged)
+    i4x w[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int r = r0 + i * RG;
+        w[i] = *reinterpret_cast<const i4x*>(base + static_cast<size_t>(r < S ? r : S - 1) * D);
+    }
     float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    const int r0 = chunk * kSumChunk;
-    for (int r = r0 + rg; r < r0 + kSumChunk && r < S; r += RG) {
-        const i4x w = *reinterpret_cast<const i4x*>(base + static_cast<size_t>(r) * D + cc * 8);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const unsigned u = static_cast<unsigned>(w[e]);
+            const unsigned u = static_cast<unsigned>(w[i][e]);
             m[2 * e] = fmaxf(m[2 * e], fabsf(half_bits_to_float(u & 0xffffu)));
             m[2 * e + 1] = fmaxf(m[2 * e + 1], fabsf(half_bits_to_float(u >> 16)));
         }
-    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) red[rg][cc * 8 + e] = m[e];
     __syncthreads();
@@ -254,11 +290,29 @@ __global__ __launch_bounds__(256) void v_quant_kernel(const uint16_t* __restrict
     const int n0 = blockIdx.x * 64;
     const size_t bk = blockIdx.y;
     const int Sp = gridDim.x * 64;
-    if (t < D) {
-        float a = 0.0f;
-        for (int i = 0; i < nchunk; ++i) a = fmaxf(a, partial[(bk * nchunk + i) * D + t]);
-        rs[t] = a == 0.0f ? 0.0f : __fdiv_rn(448.0f, a);
-        if (blockIdx.x == 0) v_scale[bk * D + t] = a == 0.0f ? 0.0f : __fdiv_rn(a, 448.0f);
+    {
+        // the chunk maxima: 256 / D threads per channel, loads unrolled so
+        // they are in flight together
+        constexpr int G = 256 / D;
+        __shared__ float gmax[G][D];
+        const int c = t % D, grp = t / D;
+        const float* src = partial + bk * static_cast<size_t>(nchunk) * D + c;
+        float a4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        int i = grp;
+        for (; i + 3 * G < nchunk; i += 4 * G) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) a4[u] = fmaxf(a4[u], src[static_cast<size_t>(i + u * G) * D]);
+        }
+        for (; i < nchunk; i += G) a4[0] = fmaxf(a4[0], src[static_cast<size_t>(i) * D]);
+        gmax[grp][c] = fmaxf(fmaxf(a4[0], a4[1]), fmaxf(a4[2], a4[3]));
+        __syncthreads();
+        if (t < D) {
+            float a = 0.0f;
+#pragma unroll
+            for (int g = 0; g < G; ++g) a = fmaxf(a, gmax[g][t]);
+            rs[t] = a == 0.0f ? 0.0f : __fdiv_rn(448.0f, a);
+            if (blockIdx.x == 0) v_scale[bk * D + t] = a == 0.0f ? 0.0f : __fdiv_rn(a, 448.0f);
+        }
     }
     __syncthreads();
     const uint16_t* base = v + bk * static_cast<size_t>(S) * D;
@@ -299,9 +353,9 @@ int launch_quantize_d(const attn_shape& s, const void* q, const void* k, int8_t*
     const int BH_kv = s.batch * s.heads_kv;
     const uint16_t* kk = static_cast<const uint16_t*>(k);
     const uint16_t* qq = static_cast<const uint16_t*>(q);
-    hipLaunchKernelGGL(k_colsum_kernel<D>, dim3(ws.nchunk, BH_kv), dim3(256), 0, st, kk, S,
+    hipLaunchKernelGGL(k_colsum_kernel<D>, dim3(ws.nchunk, BH_kv), dim3(kColsumThreads), 0, st, kk, S,
                        ws.nchunk, ws.partial);
-    hipLaunchKernelGGL(k_mean_kernel<D>, dim3(BH_kv), dim3(D), 0, st, ws.partial, S, ws.nchunk,
+    hipLaunchKernelGGL(k_mean_kernel<D>, dim3(BH_kv), dim3(D * kMeanGroups), 0, st, ws.partial, S, ws.nchunk,
                        ws.mean, k_mean);
     const int nkb = ceil_div(S, kBK), nqb = ceil_div(S, kBQ);
     hipLaunchKernelGGL((quant_block_kernel<D, kBK, true, FP8>), dim3(nkb, s.heads_kv, s.batch),
