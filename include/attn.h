@@ -89,7 +89,8 @@ size_t attn_quantize_workspace_bytes(const attn_shape* shape);
  *       tokens taken exactly (fp16 values are integer multiples of 2^-24),
  *       rounded once to fp64, divided by S in fp64, rounded to fp32.  The mean
  *       runs over all tokens also for causal attention: the shift q_i . mu is
- *       constant along each score row, so softmax is unchanged.
+ *       constant along each score row, so softmax is unchanged.  K must be
+ *       finite (with an inf or NaN in a channel its mean is unspecified).
  * smooth: ks = fp32(K) - mu (one fp32 subtraction).  Q is not smoothed.
  * quantise, per block X of BQ rows of one (b,h) of Q, or BK rows of one
  *       (b,k) of ks (the last block of a sequence may be partial):

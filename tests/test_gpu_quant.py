@@ -84,3 +84,26 @@ def test_quantize_ignores_workspace_contents_and_is_deterministic():
     torch.cuda.synchronize()
     for key in ("k_mean", "q_scale", "k_scale", "q_i8", "k_i8"):
         assert torch.equal(a[key], b[key]), key
+
+
+def test_quantize_k_mean_exact_under_cancellation():
+    """Channel sums that no fp32 summation order gets right: +-65504 pairs that
+    cancel around fp16 subnormals (2^-24), a channel of 65504 everywhere, and
+    a channel of one subnormal per token; the mean must match the oracle's
+    exact sum bit for bit across several 256-token sum chunks and a ragged
+    tail."""
+    w = small_workload(1, 2, 2, 1000, 64, False, seed=11)
+    q, k, _ = make_qkv(w)
+    S = w.seq
+    tiny = np.float16(2.0 ** -24)
+    col = np.where(np.arange(S) % 2 == 0, np.float16(65504.0), np.float16(-65504.0))
+    col[::7] = tiny                              # breaks the pairing: the sum is dominated by +-65504
+    k[0, 0, :, 0] = col
+    k[0, 0, :, 1] = np.float16(65504.0)
+    k[0, 0, :, 2] = tiny
+    k[0, 1, :, 3] = -tiny
+    k[0, 1, ::3, 3] = np.float16(-65504.0)
+    _compare(w, q, k)
+    ref = O.quantize_qk(q, k)
+    exact = k[0, 0, :, 2].astype(np.float64).sum() / S
+    assert ref["k_mean"][0, 0, 2] == np.float32(exact)
