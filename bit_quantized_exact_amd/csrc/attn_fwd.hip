@@ -213,9 +213,18 @@ __device__ __forceinline__ void score_tile(const char* ks, const typename Cfg<D,
 
 using geom::key_offset;
 
+// Waves per SIMD the register allocation targets: two (up to 256 registers
+// a lane), or three (168) at head_dim 64 where that fits without spilling
+// (INT8, and the unmasked non-causal FP16 kernel): same-run A/B on the
+// head_dim-64 video workload +4 % INT8, +2 % FP16.
+constexpr int fwd_waves(int D, bool INT8, bool CAUSAL, bool BMASK) {
+    return D == 64 && (INT8 || (!CAUSAL && !BMASK)) ? 3 : 2;
+}
+
 template <int D, bool INT8, bool CAUSAL, bool DUMP, bool QF16 = false, bool F8 = false, bool PV8 = false,
           bool BMASK = false>
-__global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kFwdThreads)
+__attribute__((amdgpu_waves_per_eu(fwd_waves(D, INT8, CAUSAL, BMASK), fwd_waves(D, INT8, CAUSAL, BMASK))))
 void fwd_kernel(const FwdParams p) {
     static_assert(!QF16 || (INT8 && !DUMP), "in-kernel Q quantisation is an INT8 forward variant");
     static_assert(!F8 || (INT8 && !DUMP && !QF16 && !PV8), "FP8 scores: standalone-quantised Q/K");
