@@ -222,7 +222,7 @@ constexpr int fwd_waves(int D, bool INT8, bool CAUSAL, bool BMASK) {
 }
 
 template <int D, bool INT8, bool CAUSAL, bool DUMP, bool QF16 = false, bool F8 = false, bool PV8 = false,
-          bool BMASK = false>
+          bool BMASK = false, bool MLDS = false>
 __global__ __launch_bounds__(kFwdThreads)
 __attribute__((amdgpu_waves_per_eu(fwd_waves(D, INT8, CAUSAL, BMASK), fwd_waves(D, INT8, CAUSAL, BMASK))))
 void fwd_kernel(const FwdParams p) {
@@ -230,6 +230,7 @@ void fwd_kernel(const FwdParams p) {
     static_assert(!F8 || (INT8 && !DUMP && !QF16 && !PV8), "FP8 scores: standalone-quantised Q/K");
     static_assert(!PV8 || (INT8 && !DUMP && !QF16 && !F8), "8-bit P.V: INT8 Q/K");
     static_assert(!BMASK || (!CAUSAL && !DUMP && !QF16 && !F8 && !PV8), "tile masks: FP16 or two-call INT8");
+    static_assert(!MLDS || BMASK, "the LDS copy of the key-tile list belongs to the tile-masked forward");
     using C = Cfg<D, INT8, F8, PV8>;
     typedef typename C::qfrag_t qfrag_t;
     typedef typename C::acc_t acc_t;
@@ -237,10 +238,12 @@ void fwd_kernel(const FwdParams p) {
     // them, one array each so that the compiler can tell the copies of
     // different stages apart), or the register path into padded tiles (the
     // score dump and the 8-bit V^T tiles).
-    // (the tile-masked variant reads its key-tile list per iteration with
-    // wave-uniform loads, which copies into LDS would turn into vector loads
-    // that drain the copy queue; it keeps the register path)
-    constexpr bool DTL = ATTN_FWD_DTL && !DUMP && !PV8 && !BMASK;
+    // (the tile-masked variant stages directly only with its key-tile list
+    // copied into LDS first (MLDS): read per iteration from global memory, the
+    // wave-uniform entry loads would become vector loads queued behind the
+    // copies into LDS; lists too long for the LDS copy keep the register path)
+    constexpr bool DTL = ATTN_FWD_DTL && !DUMP && !PV8 && (!BMASK || MLDS);
+    __shared__ int mlist[MLDS ? geom::kMaskListMax : 1];
 #ifndef ATTN_FWD_NST_F16_D128
 #define ATTN_FWD_NST_F16_D128 2
 #endif
@@ -293,14 +296,27 @@ void fwd_kernel(const FwdParams p) {
             }
             return;
         }
+        if constexpr (MLDS) {
+            // the workgroup's run of the list into LDS (count <= nkblk <= kMaskListMax,
+            // which the launch checks; clamped again here)
+            const int n = geom::imin(mrow.count, geom::kMaskListMax);
+            for (int i = tid; i < n; i += kFwdThreads) mlist[i] = p.mask_cols[mrow.base + i];
+            mrow.count = n;
+            __syncthreads();
+        }
     }
+    // list entry at position pos (positions past the end repeat the last one)
+    auto mask_entry = [&](int pos) -> int {
+        if constexpr (MLDS) return mlist[geom::imin(pos, mrow.count - 1)];
+        else return p.mask_cols[geom::mask_entry_index(mrow, pos)];
+    };
     // first key of the tile at list position pos (BMASK), else tile pos itself
     auto tile_row = [&](int pos) -> int {
-        if constexpr (BMASK) return geom::mask_entry_tile(p.mask_cols[geom::mask_entry_index(mrow, pos)], p.nkblk) * kBN;
+        if constexpr (BMASK) return geom::mask_entry_tile(mask_entry(pos), p.nkblk) * kBN;
         else return pos * kBN;
     };
     auto tile_type = [&](int pos) -> int {
-        if constexpr (BMASK) return geom::mask_entry_type(p.mask_cols[geom::mask_entry_index(mrow, pos)]);
+        if constexpr (BMASK) return geom::mask_entry_type(mask_entry(pos));
         else return CAUSAL ? 2 : 1;
     };
     const int nkt = BMASK ? mrow.count : geom::block_key_tiles(S, q0, CAUSAL);      // key tiles of the block
@@ -421,6 +437,7 @@ void fwd_kernel(const FwdParams p) {
     char* dvs[3] = {dv0, dv1, dv2};
     // K scale of key tile t (clamped to the last block; tiles past the end are never used)
     auto kscale_at = [&](int t) -> float {
+        if constexpr (BMASK) t = tile_row(t) / kBN;   // (list position -> key tile)
         return p.k_scale[bhk * p.nkblk + geom::imin(t, p.nkblk - 1)];
     };
     float ksring[3] = {1.0f, 1.0f, 1.0f};
@@ -796,11 +813,11 @@ void fwd_kernel(const FwdParams p) {
 }
 
 template <int D, bool INT8, bool CAUSAL, bool DUMP, bool QF16 = false, bool F8 = false, bool PV8 = false,
-          bool BMASK = false>
+          bool BMASK = false, bool MLDS = false>
 void launch_one(const FwdParams& p, hipStream_t st) {
     const int blocks = p.B * p.Hq * p.ntiles;
-    hipLaunchKernelGGL((fwd_kernel<D, INT8, CAUSAL, DUMP, QF16, F8, PV8, BMASK>), dim3(blocks), dim3(kFwdThreads), 0,
-                       st, p);
+    hipLaunchKernelGGL((fwd_kernel<D, INT8, CAUSAL, DUMP, QF16, F8, PV8, BMASK, MLDS>), dim3(blocks),
+                       dim3(kFwdThreads), 0, st, p);
 }
 
 template <int D>
@@ -827,10 +844,12 @@ void launch_d(FwdKind kind, bool causal, const FwdParams& p, hipStream_t st) {
                    : launch_one<D, true, false, false, false, false, true>(p, st);
             break;
         case FwdKind::kFp16Mask:
-            launch_one<D, false, false, false, false, false, false, true>(p, st);
+            p.nkblk <= geom::kMaskListMax ? launch_one<D, false, false, false, false, false, false, true, true>(p, st)
+                                          : launch_one<D, false, false, false, false, false, false, true>(p, st);
             break;
         case FwdKind::kInt8Mask:
-            launch_one<D, true, false, false, false, false, false, true>(p, st);
+            p.nkblk <= geom::kMaskListMax ? launch_one<D, true, false, false, false, false, false, true, true>(p, st)
+                                          : launch_one<D, true, false, false, false, false, false, true>(p, st);
             break;
     }
 }

@@ -139,6 +139,9 @@ __host__ __device__ inline MaskRow mask_row(int rp0, int rp1, int nnz, int nkblk
     r.count = imin(imax(rp1 - r.base, 0), imin(nkblk, imax(nnz, 0) - r.base));
     return r;
 }
+// Key tiles of a list the tile-masked forward copies into LDS (sequences up
+// to 32768 tokens); longer lists are read from global memory.
+constexpr int kMaskListMax = 512;
 // entry index of list position pos (positions past the end repeat the last; count >= 1)
 __host__ __device__ inline int mask_entry_index(const MaskRow& r, int pos) { return r.base + imin(pos, r.count - 1); }
 __host__ __device__ inline int mask_entry_tile(int e, int nkblk) { return imin(imax(e >> 2, 0), nkblk - 1); }

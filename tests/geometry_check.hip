@@ -245,6 +245,16 @@ static void check_mask_lists() {
             const int idx = mask_entry_index(r, pos);
             REQUIRE(idx >= 0 && idx < nnz, "entry index %d of %d", idx, nnz);
         }
+        // the LDS copy of a run (launched only while nkblk <= kMaskListMax):
+        // copy indices base + i, i < count, and list reads min(pos, count-1)
+        if (nkblk <= kMaskListMax) {
+            const int n = imin(r.count, kMaskListMax);
+            REQUIRE(n == r.count && n <= kMaskListMax && r.base + n <= nnz, "LDS list of %d", n);
+            for (int pos = 0; pos < n + 4; ++pos) {
+                const int li = imin(pos, n - 1);
+                REQUIRE(li >= 0 && li < kMaskListMax, "LDS list index %d", li);
+            }
+        }
         const int e = static_cast<int>(x);   // any 32-bit entry
         const int kt = mask_entry_tile(e, nkblk);
         REQUIRE(kt >= 0 && kt < nkblk, "key tile %d of %d", kt, nkblk);

@@ -129,3 +129,31 @@ def test_apb_prefill_full_size_sampled():
     assert not g8[:, :, passing].any()
     cos, rel = cos_rel_l1(g8[:, :, ~passing], exact[:, :, ~passing])
     assert cos >= INT8_COS_MIN and rel <= INT8_REL_L1_MAX, (cos, rel)
+
+
+@pytest.mark.parametrize("S", [32768, 32769])
+def test_apb_mask_long_lists(S):
+    """Key-tile lists of up to 512 tiles are copied into LDS and staged
+    directly (S = 32768); longer ones (S = 32769: 513 key tiles) are read from
+    global memory on the register-staged path.  Both must reproduce the causal
+    kernel bit for bit outside the passing rows and give zero rows inside."""
+    anchor, passing = 1024, 2048
+    w = small_workload(1, 2, 1, S, 64, False, 900 + S % 7)
+    q, k, v = make_qkv(w)
+    m = A.apb_block_mask(S, anchor, passing)
+    csr = A.block_mask_csr(S, m)
+    case(f"fwd_*_masked long list S={S} nnz={csr['nnz']}")
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    o16 = A.fwd_fp16_masked(qd, kd, vd, csr)
+    qz = A.quantize_qk(qd, kd)
+    o8 = A.fwd_int8_masked(qz, vd, csr)
+    c16 = A.fwd_fp16(qd, kd, vd, causal=True)
+    c8 = A.fwd_int8(qz, vd, causal=True)
+    torch.cuda.synchronize()
+    keep = torch.from_numpy(np.r_[0:anchor, anchor + passing:S]).cuda()
+    assert torch.equal(o16[:, :, keep], c16[:, :, keep]) and torch.equal(o8[:, :, keep], c8[:, :, keep])
+    assert not o16[:, :, anchor:anchor + passing].any() and not o8[:, :, anchor:anchor + passing].any()
+    # a few rows against the oracle (exact causal attention over the visible keys)
+    rows = np.r_[0, anchor - 1, anchor + passing, S // 2, S - 1]
+    exact = O.attention(q, k, v, causal=True, rows=rows)
+    assert np.abs(host(o16).astype(np.float64)[:, :, rows] - exact).max() <= FP16_MAX_ABS
