@@ -66,6 +66,11 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (HBM counter calibration)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the KV-cache decode measurement (one JSON line; for profiling)")
+    ap.add_argument("--decode-reps", type=int, default=20, help="timed calls per decode kernel")
+    ap.add_argument("--clock-warm-ms", type=float, default=CLOCK_WARM_MS,
+                    help="untimed busy time before each timed section")
     return ap.parse_args()
 
 
@@ -100,10 +105,14 @@ def counters_for(kernel_tag: str, workload: str):
 CLOCK_WARM_MS = 300.0
 
 
-def clock_warm(fn, min_ms=CLOCK_WARM_MS, batch=4):
-    """Call fn (batches of `batch` calls) until at least min_ms of wall time has
-    passed with the GPU busy; returns the number of calls (untimed)."""
+def clock_warm(fn, min_ms=None, batch=4):
+    """Call fn (batches of `batch` calls) until at least min_ms (default
+    CLOCK_WARM_MS) of wall time has passed with the GPU busy; returns the
+    number of calls (untimed)."""
     import torch
+
+    if min_ms is None:
+        min_ms = CLOCK_WARM_MS
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -301,7 +310,7 @@ def run_workload(name, steps, warmup, cpu=False, cpu_seconds=15.0):
     return rec
 
 
-def run_decode(name="decode_gqa", reps=20):
+def run_decode(name="decode_gqa", reps=20, warm_ms=None):
     """KV-cache decode (one query per sequence over a cached context): the
     INT8 kernel (cache quantised once beforehand) and the FP16 kernel, each
     timed with HIP events; HBM-bound, so reported as GB/s of algorithmic bytes
@@ -323,7 +332,7 @@ def run_decode(name="decode_gqa", reps=20):
     f16 = lambda: A.decode_fp16(qd, kd, vd, causal=w.causal, out=o16, workspace=ws8)
     res = {}
     for tag, fn in (("int8", f8), ("fp16", f16)):
-        clock_warm(fn, batch=16)
+        clock_warm(fn, min_ms=CLOCK_WARM_MS if warm_ms is None else warm_ms, batch=16)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(reps):
@@ -447,11 +456,16 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
+    global CLOCK_WARM_MS
+    CLOCK_WARM_MS = args.clock_warm_ms
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the hot path "
               "shards by kv-head groups with no communication, so it is measured per GPU.",
               file=sys.stderr)
         sys.exit(2)
+    if args.decode_only:
+        print(json.dumps(run_decode(reps=args.decode_reps)), flush=True)
+        return
     if args.all_workloads:
         from bit_quantized_exact_amd.inputs import WORKLOADS
         for name in WORKLOADS:
