@@ -249,8 +249,11 @@ void decode_kernel(const DecParams p) {
 #pragma unroll
         for (int r = 1; r < 16; ++r) mx = __builtin_fmaxf(mx, sv[r]);
         const float m_tile = (INT8 ? row_max(mx) - kI8Bias : row_max(mx)) * c;
-        if (__ballot(m_tile > m_run + kLazy)) {
-            const float m_new = __builtin_fmaxf(m_run, m_tile);
+        const bool raise = m_tile > m_run + kLazy;
+        if (__ballot(raise)) {
+            // (each row decides for itself: a row's result never depends on the
+            // scores of the other rows of the wave)
+            const float m_new = raise ? m_tile : m_run;
             // (a row that has seen no key yet has an empty state: alpha = 0 avoids
             // exp2(-inf - -inf) when the other rows of the wave raise their maximum)
             const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);

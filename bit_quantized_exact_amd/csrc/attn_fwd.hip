@@ -629,8 +629,11 @@ void fwd_kernel(const FwdParams p) {
                 // (the biased maximum minus the bias is exact: both lie in [2^23, 2^24))
                 const float m_tile = (kBiased ? row_max(mx) - kI8Bias : row_max(mx)) * c;
                 // (8-bit P needs p <= 1: no lazy headroom there)
-                if (__ballot(m_tile > m_run + (PV8 ? 0.0f : kLazy))) {
-                    const float m_new = fmaxf(m_run, m_tile);
+                const bool raise = m_tile > m_run + (PV8 ? 0.0f : kLazy);
+                if (__ballot(raise)) {
+                    // (each row decides for itself: a row's result never depends on
+                    // the scores of the other rows of the wave)
+                    const float m_new = raise ? m_tile : m_run;
                     // (with tile masks a row may have seen no key yet: its state is
                     // empty, alpha = 0 avoids exp2(-inf - -inf))
                     const float alpha = BMASK && m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);

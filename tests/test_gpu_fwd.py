@@ -246,6 +246,52 @@ def test_gqa_equals_mha_on_repeated_kv_gpu():
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_causal_future_keys_have_no_effect(D):
+    """Causal mask (MHA-GQA article, §2.3): perturbing the keys and values of
+    positions after row i leaves rows 0..i bit-identical (FP16 path, whose
+    inputs are used as given); the INT8 path is checked with the quantised
+    tensors held fixed, so that only the masked products change."""
+    S, cut = 300, 173
+    w = small_workload(1, 4, 2, S, D, True, seed=91 + D)
+    q, k, v = make_qkv(w)
+    k2, v2 = k.copy(), v.copy()
+    rng = np.random.default_rng(5)
+    k2[:, :, cut:] = rng.standard_normal(k2[:, :, cut:].shape).astype(np.float16) * 8
+    v2[:, :, cut:] = -v2[:, :, cut:] + 1
+    case(f"causal future keys D={D}")
+    a = A.fwd_fp16(dev(q), dev(k), dev(v), causal=True)
+    b = A.fwd_fp16(dev(q), dev(k2), dev(v2), causal=True)
+    qz = A.quantize_qk(dev(q), dev(k))
+    qz2 = dict(qz)
+    k8 = qz["k_i8"].clone()
+    k8[:, :, cut:] = torch.randint(-127, 128, k8[:, :, cut:].shape, dtype=torch.int8, device=k8.device)
+    qz2["k_i8"] = k8
+    c = A.fwd_int8(qz, dev(v), causal=True)
+    d = A.fwd_int8(qz2, dev(v2), causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a[:, :, :cut], b[:, :, :cut]) and not torch.equal(a, b)
+    assert torch.equal(c[:, :, :cut], d[:, :, :cut]) and not torch.equal(c, d)
+
+
+def test_kv_head_change_reaches_only_its_group():
+    """GQA (MHA-GQA article, §5.1): changing K/V of kv-head 1 changes exactly
+    the q-heads mapped to it, for the default and an explicit map."""
+    w = small_workload(1, 8, 4, 200, 128, False, seed=97)
+    q, k, v = make_qkv(w)
+    k2, v2 = k.copy(), v.copy()
+    k2[:, 1] = k2[:, 1][:, ::-1]
+    v2[:, 1] = v2[:, 1] * 2
+    for kv_map in (None, [3, 1, 0, 1, 2, 2, 1, 0]):
+        case(f"kv-head group isolation map={kv_map}")
+        a = host(A.fwd_fp16(dev(q), dev(k), dev(v), kv_head_map=kv_map))
+        b = host(A.fwd_fp16(dev(q), dev(k2), dev(v2), kv_head_map=kv_map))
+        heads = [h for h in range(8) if (h // 2 if kv_map is None else kv_map[h]) == 1]
+        for h in range(8):
+            same = np.array_equal(a[:, h], b[:, h])
+            assert same == (h not in heads), (kv_map, h)
+
+
 def test_custom_scale_and_sageattn_wrapper():
     w = small_workload(1, 4, 2, 200, 64, False, seed=81)
     q, k, v = make_qkv(w)
