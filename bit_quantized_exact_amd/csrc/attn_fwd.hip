@@ -71,7 +71,6 @@ typedef float f16x __attribute__((ext_vector_type(16)));
 typedef int i16x __attribute__((ext_vector_type(16)));
 typedef int i4x __attribute__((ext_vector_type(4)));
 typedef int i8x __attribute__((ext_vector_type(8)));
-typedef int i2x __attribute__((ext_vector_type(2)));
 typedef __fp16 tr4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
 typedef __attribute__((address_space(3))) tr4 lds_tr4;
 
@@ -86,20 +85,19 @@ constexpr float kI8Bias = 12582912.0f;
 constexpr float kLazy = 8.0f;   // log2 headroom before the running max is raised
 
 // F8: the 8-bit Q/K codes are E4M3 (FP8 alternative) instead of INT8.
-// PV8: the 8-bit P.V ablation (E4M3 P, E4M3 V stored as V^T tiles).
+// PV8: the 8-bit P.V ablation (E4M3 P, E4M3 V stored as V^T tiles, staged
+// directly into LDS only).
 template <int D, bool INT8, bool F8 = false, bool PV8 = false>
 struct Cfg : geom::Stage<D, INT8> {
     using G = geom::Stage<D, INT8>;
     using G::KELT, G::KROWG, G::KCPR, G::VCPR, G::KPT, G::QSTEPS;
     static constexpr int KROW = KROWG + 16;                    // K row bytes in LDS
-    // V tile in LDS: 64 key rows of 2D bytes (+ padding), or for PV8 D rows
-    // of 64 key bytes (+ padding) split into the two lane halves' key sets
-    static constexpr int VROW = PV8 ? 64 + 16 : 2 * D + 64;
-    static constexpr int VPT = PV8 ? geom::StageV8<D>::VPT : G::VPT;
+    static constexpr int VROW = 2 * D + 64;                    // V row bytes in LDS (register staging)
+    static constexpr int VPT = G::VPT;
     static constexpr int KBYTES = kBN * KROW;
-    static constexpr int VBYTES = (PV8 ? D : kBN) * VROW;
+    static constexpr int VBYTES = kBN * VROW;
     static constexpr int KSTAGE = kBN * KROWG;                 // unpadded tiles (direct-to-LDS staging)
-    static constexpr int VSTAGE = kBN * 2 * D;
+    static constexpr int VSTAGE = PV8 ? D * kBN : kBN * 2 * D; // (PV8: D rows of 64 key codes)
     static constexpr int DT = D / 32;                          // 32-row d tiles of O^T
     static_assert(kBN * KCPR % kFwdThreads == 0 && kBN * VCPR % kFwdThreads == 0, "tile split");
     static_assert(geom::kTileM == kBM && geom::kTileN == kBN && geom::kThreads == kFwdThreads, "geometry");
@@ -242,7 +240,8 @@ void fwd_kernel(const FwdParams p) {
     // copied into LDS first (MLDS): read per iteration from global memory, the
     // wave-uniform entry loads would become vector loads queued behind the
     // copies into LDS; lists too long for the LDS copy keep the register path)
-    constexpr bool DTL = ATTN_FWD_DTL && !DUMP && !PV8 && (!BMASK || MLDS);
+    constexpr bool DTL = ATTN_FWD_DTL && !DUMP && (!BMASK || MLDS);
+    static_assert(!PV8 || DTL, "the 8-bit P.V variant stages its V^T tiles directly into LDS");
     __shared__ int mlist[MLDS ? geom::kMaskListMax : 1];
 #ifndef ATTN_FWD_NST_F16_D128
 #define ATTN_FWD_NST_F16_D128 2
@@ -346,17 +345,6 @@ void fwd_kernel(const FwdParams p) {
         }
     };
     auto gload_v = [&](int n0, i4x (&dst)[C::VPT]) {
-        if constexpr (PV8) {
-            const char* base = vg + geom::v8_tile_col(n0, p.nkblk);
-#pragma unroll
-            for (int i = 0; i < C::VPT; ++i) {
-                const int c = tid + kFwdThreads * i;
-                const uint32_t off = static_cast<uint32_t>(c / geom::kV8ChunksPerRow) * vt_stride +
-                                     (c % geom::kV8ChunksPerRow) * 16;
-                dst[i] = *reinterpret_cast<const i4x*>(base + off);
-            }
-            return;
-        }
         const int first = geom::tile_first_row(n0, S);
         const char* base = vg + static_cast<size_t>(first) * C::VROWG;
 #pragma unroll
@@ -377,23 +365,6 @@ void fwd_kernel(const FwdParams p) {
     };
     auto sstore_v = [&](int stage, const i4x (&src)[C::VPT]) {
         char* vs = vbuf(stage);
-        if constexpr (PV8) {
-            // chunk part q16 of row d holds keys 16 q16 .. +15; dwords 0 and 2
-            // (keys +0..3, +8..11) belong to lanes 0-31, dwords 1 and 3 to
-            // lanes 32-63.  Each half is stored in the order its MFMA operand
-            // slots take the keys: slot mt*16 + r <-> key_offset(mt, r) + 4 g.
-#pragma unroll
-            for (int i = 0; i < C::VPT; ++i) {
-                const int c = tid + kFwdThreads * i;
-                const int d = c / geom::kV8ChunksPerRow, q16 = c % geom::kV8ChunksPerRow;
-                char* row = vs + d * C::VROW + (q16 >> 1) * 16 + (q16 & 1) * 8;
-                const i2x lo = {src[i][0], src[i][2]};
-                const i2x hi = {src[i][1], src[i][3]};
-                *reinterpret_cast<i2x*>(row) = lo;
-                *reinterpret_cast<i2x*>(row + 32) = hi;
-            }
-            return;
-        }
 #pragma unroll
         for (int i = 0; i < C::VPT; ++i) {
             const int c = tid + kFwdThreads * i;
@@ -420,7 +391,23 @@ void fwd_kernel(const FwdParams p) {
                                              16, 0, 0);
         }
     };
+    using D8 = geom::Dtl8<D>;
+    constexpr int VNI = PV8 ? D8::NI : DV::NI;   // V copy instructions per wave per tile
     auto dtl_v = [&](int n0, char* st) __attribute__((always_inline)) {
+        if constexpr (PV8) {
+            // D rows of 64 key codes of the V^T tile at column v8_tile_col
+            const char* base = vg + geom::v8_tile_col(n0, p.nkblk);
+#pragma unroll
+            for (int i = 0; i < D8::NI; ++i) {
+                const int r = D8::slot_row(wave, i, lane);
+                const int c = D8::slot_chunk(wave, i, lane) ^ D8::swz(r);
+                const uint32_t off = static_cast<uint32_t>(r) * vt_stride + c * 16;
+                __builtin_amdgcn_global_load_lds(base + off,
+                                                 (__attribute__((address_space(3))) void*)(st + (wave_s * D8::NI + i) * 1024),
+                                                 16, 0, 0);
+            }
+            return;
+        }
         const int first = geom::tile_first_row(n0, S);
         const char* base = vg + static_cast<size_t>(first) * C::VROWG;
 #pragma unroll
@@ -667,22 +654,36 @@ void fwd_kernel(const FwdParams p) {
                     for (int r = 0; r < 16; ++r) psum += pv[mt][r];
                 l_run += psum;
                 if constexpr (PV8) {
-                    // ---- O^T += V8^T P8^T: E4M3(448 p) in operand slot
-                    // mt*16 + r, V codes from the split rows (one MFMA per d tile)
-                    i8x pb8;
+                    // ---- O^T += V8^T P8^T (one MFMA per d tile).  Dword k of
+                    // the E4M3(448 p) codes of lane half g holds the tile's
+                    // 4-key group (k >> 2) * 8 + (k & 3) * 2 + g (the score
+                    // layout); exchanging dwords 4..7 of half 0 with dwords
+                    // 0..3 of half 1 leaves half g the groups 8g .. 8g+7 in
+                    // order, i.e. keys 32g .. 32g+31, which is what it reads
+                    // from the natural V^T row.
+                    int pw[8];
 #pragma unroll
                     for (int k = 0; k < 8; ++k) {
                         const float* q = &pv[k >> 2][(k & 3) * 4];
                         int w = __builtin_amdgcn_cvt_pk_fp8_f32(q[0] * 448.0f, q[1] * 448.0f, 0, false);
                         w = __builtin_amdgcn_cvt_pk_fp8_f32(q[2] * 448.0f, q[3] * 448.0f, w, true);
-                        pb8[k] = w;
+                        pw[k] = w;
+                    }
+                    i8x pb8;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const auto x = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(pw[i]),
+                                                                        static_cast<unsigned>(pw[4 + i]), false, false);
+                        pb8[2 * i] = static_cast<int>(x[0]);
+                        pb8[2 * i + 1] = static_cast<int>(x[1]);
                     }
                     const char* vs = vsc;
 #pragma unroll
                     for (int dt = 0; dt < C::DT; ++dt) {
-                        const char* row = vs + (dt * 32 + l32) * C::VROW + g * 32;
-                        const i4x a0 = *reinterpret_cast<const i4x*>(row);
-                        const i4x a1 = *reinterpret_cast<const i4x*>(row + 16);
+                        const int r = dt * 32 + l32;
+                        const char* row = vs + r * kBN;
+                        const i4x a0 = *reinterpret_cast<const i4x*>(row + (((2 * g) ^ D8::swz(r)) << 4));
+                        const i4x a1 = *reinterpret_cast<const i4x*>(row + (((2 * g + 1) ^ D8::swz(r)) << 4));
                         const i8x a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
                         oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb8, oacc[dt], 0, 0, 0, 0, 0, 0);
                     }
@@ -757,7 +758,7 @@ void fwd_kernel(const FwdParams p) {
         auto dstep = [&](int j, auto j_tag) __attribute__((always_inline)) {
             constexpr int J = decltype(j_tag)::value;
             const float ksj = ksring[J];
-            lds_stage_barrier<NST == 3 ? DK::NI + DV::NI + (INT8 ? 1 : 0) : 0>();
+            lds_stage_barrier<NST == 3 ? DK::NI + VNI + (INT8 ? 1 : 0) : 0>();
             dtl_k(tile_row(j + NST), dks[J]);
             if constexpr (INT8) ksring[J] = kscale_at(j + NST);
             dtl_v(tile_row(j + NST - 1), dvs[(J + NST - 1) % NST]);

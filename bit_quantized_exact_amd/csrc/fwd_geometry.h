@@ -113,14 +113,19 @@ struct Dtl {
 // 8-bit V of the P.V ablation: V^T codes [B*Hkv, D, Sp], Sp = 64 * nkblk.
 // A key tile at n0 is D rows of 64 bytes starting at column
 // v8_tile_col(n0, nkblk); tiles prefetched past the end are clamped to the
-// last tile (always inside the buffer).  Thread chunk c (16 bytes) covers row
-// d = c / 4, bytes (c % 4) * 16 of the tile.
-constexpr int kV8ChunksPerRow = 4;
+// last tile (always inside the buffer).  It is copied straight into an
+// unpadded LDS stage of D rows of 64 bytes whose 16-byte chunks are
+// XOR-swizzled by row group (the 32-byte reads of the two lane halves are
+// then free of bank conflicts); instruction i of wave w fills stage bytes
+// (w*NI + i)*1024 .. +1023.
 __host__ __device__ inline int v8_tile_col(int n0, int nkblk) { return imin(n0, (nkblk - 1) * kTileN); }
 template <int D>
-struct StageV8 {
-    static constexpr int VPT = D * kV8ChunksPerRow / kThreads;   // 16-byte chunks per thread
-    static_assert(D * kV8ChunksPerRow % kThreads == 0, "tile split");
+struct Dtl8 {
+    static constexpr int NI = D * kTileN / 1024 / 4;   // instructions per wave per tile
+    static_assert(D * kTileN % 4096 == 0, "tile split");
+    __host__ __device__ static constexpr int swz(int r) { return (r >> 2) & 3; }
+    __host__ __device__ static constexpr int slot_row(int w, int i, int lane) { return ((w * NI + i) * 64 + lane) / 4; }
+    __host__ __device__ static constexpr int slot_chunk(int w, int i, int lane) { return ((w * NI + i) * 64 + lane) % 4; }
 };
 
 // Tile-mask lists: for each query tile, a run of entries e = (key tile << 2)

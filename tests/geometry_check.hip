@@ -114,9 +114,9 @@ static void check_shape(int B, int Hq, int S, bool causal, bool dump, int tile_l
                 vn0.push_back(depth == 2 ? v_load_row<2>(j) : v_load_row<1>(j));
             }
         }
-        // direct-to-LDS staging (all non-dump variants except the 8-bit V^T
-        // one): every (wave, instruction, lane) slot of every copied tile
-        if (!dump && !pv8) {
+        // direct-to-LDS staging (all non-dump variants): every (wave,
+        // instruction, lane) slot of every copied tile
+        if (!dump) {
             const int nst = (!INT8 && D == 128) ? 2 : 3;
             std::vector<int> dk, dvv;
             for (int t = 0; t < nst; ++t) dk.push_back(t * kTileN);
@@ -159,7 +159,32 @@ static void check_shape(int B, int Hq, int S, bool causal, bool dump, int tile_l
                 for (int v : seen_slot) REQUIRE(v == 1, "dtl slot written %d times", v);
             };
             for (int n0 : dk) check_tile(n0, St::KROWG, qk_head_bytes, false);
-            for (int n0 : dvv) check_tile(n0, St::VROWG, v_head_bytes, true);
+            if (!pv8) {
+                for (int n0 : dvv) check_tile(n0, St::VROWG, v_head_bytes, true);
+            } else {
+                // 8-bit V^T tiles: D rows of 64 codes at column v8_tile_col, row stride Sp
+                const int Sp = nkblk * kTileN;
+                const size_t vt_head_bytes = static_cast<size_t>(D) * Sp;
+                for (int n0 : dvv) {
+                    const int col = v8_tile_col(n0, nkblk);
+                    REQUIRE(col >= 0 && col % kTileN == 0 && col + kTileN <= Sp, "v8 column %d (n0 %d, Sp %d)", col, n0, Sp);
+                    std::vector<int> seen(static_cast<size_t>(D) * 4, 0);
+                    for (int w = 0; w < 4; ++w)
+                        for (int i = 0; i < Dtl8<D>::NI; ++i)
+                            for (int lane = 0; lane < 64; ++lane) {
+                                const int r = Dtl8<D>::slot_row(w, i, lane), pc = Dtl8<D>::slot_chunk(w, i, lane);
+                                const int c = pc ^ Dtl8<D>::swz(r);
+                                REQUIRE(r >= 0 && r < D && pc >= 0 && pc < 4 && c >= 0 && c < 4, "v8 slot r %d pc %d c %d", r, pc, c);
+                                REQUIRE((w * Dtl8<D>::NI + i) * 1024 + lane * 16 == r * kTileN + pc * 16, "v8 lds byte");
+                                seen[static_cast<size_t>(r) * 4 + pc] += 1;
+                                const long long off32 = static_cast<long long>(r) * Sp + c * 16;
+                                REQUIRE(off32 < (1LL << 32), "v8 lane offset %lld", off32);
+                                const size_t off = static_cast<size_t>(col) + static_cast<size_t>(off32);
+                                REQUIRE(off + 16 <= vt_head_bytes, "v8 byte %zu of %zu", off, vt_head_bytes);
+                            }
+                    for (int v : seen) REQUIRE(v == 1, "v8 slot written %d times", v);
+                }
+            }
         }
         for (int n0 : kn0) {
             const int first = tile_first_row(n0, S);
@@ -175,26 +200,7 @@ static void check_shape(int B, int Hq, int S, bool causal, bool dump, int tile_l
                     REQUIRE(off + 16 <= qk_head_bytes, "k byte %zu of %zu", off, qk_head_bytes);
                 }
         }
-        if (pv8) {
-            const int Sp = nkblk * kTileN;
-            const size_t vt_head_bytes = static_cast<size_t>(D) * Sp;
-            for (int n0 : vn0) {
-                const int col = v8_tile_col(n0, nkblk);
-                REQUIRE(col >= 0 && col % kTileN == 0 && col + kTileN <= Sp, "v8 column %d (n0 %d, Sp %d)", col, n0, Sp);
-                for (int tid = 0; tid < kThreads; ++tid)
-                    for (int i = 0; i < StageV8<D>::VPT; ++i) {
-                        const int cidx = tid + kThreads * i;
-                        const int d = cidx / kV8ChunksPerRow, part = cidx % kV8ChunksPerRow;
-                        REQUIRE(d >= 0 && d < D, "v8 row %d", d);
-                        const long long off32 = static_cast<long long>(d) * Sp + part * 16;
-                        REQUIRE(off32 < (1LL << 32), "v8 lane offset %lld", off32);
-                        const size_t off = static_cast<size_t>(col) + static_cast<size_t>(off32);
-                        REQUIRE(off + 16 <= vt_head_bytes, "v8 byte %zu of %zu", off, vt_head_bytes);
-                        REQUIRE(part * 16 + 16 <= kTileN, "v8 chunk %d", part);
-                    }
-            }
-            vn0.clear();
-        }
+        if (pv8) vn0.clear();   // (its V tiles are staged directly, checked above)
         for (int n0 : vn0) {
             const int first = tile_first_row(n0, S);
             REQUIRE(first >= 0 && first <= S - 1, "v first row %d", first);
