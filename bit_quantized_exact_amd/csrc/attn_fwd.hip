@@ -40,8 +40,8 @@
 //     three (FP16 at D = 128: two) stages per tile kind; the stages are
 //     unpadded and XOR-swizzled in 16-byte chunks so that the MFMA operand
 //     reads and the transposing reads are free of bank conflicts.  The
-//     INT32 score dump, the 8-bit P.V variant and the tile-masked variant
-//     stage through registers into padded rows instead.
+//     INT32 score dump, and tile-masked lists longer than the LDS copy of
+//     the list holds, stage through registers into padded rows instead.
 //   * Lazy rescaling: the running maximum is only raised (and O, l rescaled)
 //     when a tile's maximum exceeds it by more than 2^8; otherwise the stale
 //     maximum is kept, weights stay <= 2^8 (exact in fp16 range), and the
