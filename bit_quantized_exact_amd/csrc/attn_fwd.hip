@@ -235,7 +235,7 @@ void fwd_kernel(const FwdParams p) {
     // Staging: direct-to-LDS copies into unpadded swizzled stages (NST of
     // them, one array each so that the compiler can tell the copies of
     // different stages apart), or the register path into padded tiles (the
-    // score dump and the 8-bit V^T tiles).
+    // score dump, and tile-mask lists too long for their LDS copy).
     // (the tile-masked variant stages directly only with its key-tile list
     // copied into LDS first (MLDS): read per iteration from global memory, the
     // wave-uniform entry loads would become vector loads queued behind the
