@@ -29,8 +29,14 @@ TFLOPS and as a fraction of MI355X's published dense MFMA peak (fp16
 CPU oracle (fp64, plain loops) on a bounded sample of the same workload's
 query rows, on this machine's host cores.
 
+Each timed section is preceded by untimed calls for CLOCK_WARM_MS of busy
+time (the clocks ramp up after the GPU idled while the CPU drew the inputs),
+then the W warm-up steps, then exactly K timed steps.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-       [--all-workloads] [--no-cpu]
+       [--all-workloads] [--no-cpu] [--clock-warm-ms MS]
+       python bench.py --decode-only [--decode-reps N]      (profiling)
+       python bench.py --copy-calibration BYTES             (HBM counter scale)
 """
 from __future__ import annotations
 
