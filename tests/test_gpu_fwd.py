@@ -347,3 +347,41 @@ def test_fused_q_workloads_bitwise_and_accuracy(name):
     rows = sample_rows(w.seq, 16, seed=w.seed + 7)
     cos, rel = cos_rel_l1(host(o)[:, :, rows], O.attention(q, k, v, causal=w.causal, rows=rows))
     assert cos >= INT8_COS_MIN and rel <= INT8_REL_L1_MAX, (cos, rel)
+
+
+def _random_configs(n=12, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        hkv = int(rng.choice([1, 2, 4]))
+        group = int(rng.choice([1, 2, 4, 8]))
+        mapped = bool(rng.integers(0, 2)) and group > 1
+        out.append(dict(B=int(rng.integers(1, 4)), Hq=hkv * group, Hkv=hkv, S=int(rng.integers(1, 1501)),
+                        D=int(rng.choice([64, 128])), causal=bool(rng.integers(0, 2)), mapped=mapped,
+                        seed=3000 + i))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_configs(), ids=lambda c: "B{B}-H{Hq}x{Hkv}-S{S}-D{D}-{c}{m}".format(
+    c="causal" if c["causal"] else "full", m="-map" if c["mapped"] else "", **c))
+def test_random_shapes_fp16_int8_fused(cfg):
+    """Seeded random shapes (batch, GQA groups, explicit maps, any length up to
+    1500, both head dims, both masks): FP16 and INT8 paths against the oracle on
+    up to 96 rows, and the fused-Q path bit for bit against the two-call path."""
+    w = small_workload(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["S"], cfg["D"], cfg["causal"], cfg["seed"])
+    q, k, v = make_qkv(w)
+    kv_map = None
+    if cfg["mapped"]:
+        kv_map = [int(x) for x in np.random.default_rng(cfg["seed"]).integers(0, cfg["Hkv"], cfg["Hq"])]
+    S = cfg["S"]
+    rng = np.random.default_rng(cfg["seed"] + 1)
+    rows = np.unique(np.r_[0, S - 1, rng.integers(0, S, min(S, 94))]) if S > 96 else None
+    _fp16_check(w, q, k, v, rows=rows, kv_map=kv_map)
+    _int8_check(w, q, k, v, rows=rows, kv_map=kv_map)
+    case(f"fused vs two-call {w.name} map={kv_map}")
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    qz = A.quantize_qk(qd, kd)
+    a = A.fwd_int8(qz, vd, causal=w.causal, kv_head_map=kv_map)
+    b = A.fwd_int8_fused_q(qd, A.quantize_k(kd), vd, causal=w.causal, kv_head_map=kv_map)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
