@@ -281,7 +281,6 @@ __global__ __launch_bounds__(256) void v_quant_kernel(const uint16_t* __restrict
                                                       uint8_t* __restrict__ vt,
                                                       float* __restrict__ v_scale) {
     constexpr int CPR = D / 8;                 // 16-byte chunks per V row
-    constexpr int IN_PER = 64 * CPR / 256;     // input chunks per thread
     constexpr int OUT_PER = D * 4 / 256;       // 16-byte output chunks per thread
     constexpr int TROW = 64 + 16;              // transposed tile row bytes in LDS
     __shared__ float rs[D];
@@ -315,23 +314,31 @@ __global__ __launch_bounds__(256) void v_quant_kernel(const uint16_t* __restrict
         }
     }
     __syncthreads();
+    // Codes into the transposed tile: a unit is 4 consecutive rows x one
+    // 16-byte column chunk (8 channels); the 4 codes of a channel are one
+    // dword of its tile row (the 16 units of a chunk column write 16
+    // consecutive dwords: no LDS bank conflicts).  Rows past the sequence
+    // give code 0.
     const uint16_t* base = v + bk * static_cast<size_t>(S) * D;
+    for (int u = t; u < 16 * CPR; u += 256) {
+        const int r0 = (u % 16) * 4, cc = u / 16;
+        i4x w[4];
 #pragma unroll
-    for (int i = 0; i < IN_PER; ++i) {
-        const int c = t + 256 * i;
-        const int row = c / CPR, cc = c % CPR;
-        i4x w = {0, 0, 0, 0};
-        if (n0 + row < S) w = *reinterpret_cast<const i4x*>(base + static_cast<size_t>(n0 + row) * D + cc * 8);
+        for (int j = 0; j < 4; ++j) {
+            w[j] = i4x{0, 0, 0, 0};
+            if (n0 + r0 + j < S) w[j] = *reinterpret_cast<const i4x*>(base + static_cast<size_t>(n0 + r0 + j) * D + cc * 8);
+        }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const unsigned u = static_cast<unsigned>(w[e]);
-            const int ch = cc * 8 + 2 * e;
-            const float x0 = half_bits_to_float(u & 0xffffu), x1 = half_bits_to_float(u >> 16);
-            // (each value converted as both halves of a pair: the byte is then the same in either slot)
-            const unsigned lo = e4m3_pair(x0, x0, rs[ch]) & 0xffu;
-            const unsigned hi = e4m3_pair(x1, x1, rs[ch + 1]) & 0xffu;
-            tile[ch * TROW + row] = static_cast<uint8_t>(lo);
-            tile[(ch + 1) * TROW + row] = static_cast<uint8_t>(hi);
+        for (int e = 0; e < 8; ++e) {
+            const int ch = cc * 8 + e;
+            float x[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const unsigned word = static_cast<unsigned>(w[j][e >> 1]);
+                x[j] = half_bits_to_float((e & 1) ? (word >> 16) : (word & 0xffffu));
+            }
+            const unsigned code = e4m3_pair(x[0], x[1], rs[ch]) | (e4m3_pair(x[2], x[3], rs[ch]) << 16);
+            *reinterpret_cast<unsigned*>(tile + ch * TROW + r0) = code;
         }
     }
     __syncthreads();
