@@ -771,7 +771,6 @@ void fwd_kernel(const FwdParams p) {
                 dstep(j + 1, std::integral_constant<int, 1>{});
                 if constexpr (NST == 3) dstep(j + 2, std::integral_constant<int, 2>{});
             }
-            lds_stage_barrier<0>();   // no copy may still be landing when the workgroup ends
         } else if constexpr (DEPTH == 2) {
             const int iters = geom::loop_iterations<2>(nkt);
             for (int j = 0; j < iters; j += 2) {
@@ -813,6 +812,9 @@ void fwd_kernel(const FwdParams p) {
                 }
             if (p.lse && g == 0) p.lse[bhq * S + qi] = (m_run + __builtin_log2f(l_tot)) * kLn2;
         }
+        // no copy into LDS may still be landing when the workgroup ends (the
+        // last iterations' copies of tiles past the end drain under the stores)
+        if constexpr (DTL) lds_stage_barrier<0>();
     }
 }
 
