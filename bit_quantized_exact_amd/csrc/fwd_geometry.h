@@ -25,14 +25,9 @@ struct BlockCoord {
     int qt;   // query tile
 };
 
-// Hardware block id -> (batch, head position, query tile).  Consecutive
-// hardware ids go round-robin over the 8 XCDs; the renumbering gives each XCD
-// a contiguous range of logical ids.  Causal launches take the heaviest query
-// tiles first.  Bijective on [0, nblk).
-__host__ __device__ inline BlockCoord decode_block(int bid, int nblk, int Hq, int ntiles,
-                                                   int tile_lo, bool heavy_first) {
-    const int per = nblk >> 3, rem = nblk & 7, xcd = bid & 7;
-    const int L = xcd * per + imin(xcd, rem) + (bid >> 3);
+// Logical work item -> (batch, head position, query tile).  Causal launches
+// take the heaviest query tiles of a head first.  Bijective on [0, nitems).
+__host__ __device__ inline BlockCoord decode_item(int L, int Hq, int ntiles, int tile_lo, bool heavy_first) {
     const int per_b = Hq * ntiles;
     BlockCoord c;
     c.b = L / per_b;
@@ -41,6 +36,43 @@ __host__ __device__ inline BlockCoord decode_block(int bid, int nblk, int Hq, in
     const int rank = rb - c.pos * ntiles;
     c.qt = tile_lo + (heavy_first ? (ntiles - 1 - rank) : rank);
     return c;
+}
+
+// Persistent schedule of the work items over the launch's workgroups.
+// Consecutive hardware ids go round-robin over the 8 XCDs: XCD x gets a
+// contiguous range of logical items (neighbouring heads share K/V in its
+// L2) and its K workgroups walk that range in blocks of K, workgroup k
+// taking slot k of even blocks and slot K-1-k of odd ones (a snake, which
+// evens out the per-workgroup sums of the heaviest-first causal order).
+// Every item is visited exactly once when grid >= min(8, nitems) and
+// grid <= nitems; with grid == nitems each workgroup takes one item.
+struct Sched {
+    int first;   // first logical item of this XCD's range
+    int count;   // items in the range
+    int k;       // this workgroup's index on its XCD
+    int K;       // workgroups on this XCD
+};
+__host__ __device__ inline Sched make_sched(int bid, int grid, int nitems) {
+    const int x = bid & 7;
+    const int per = nitems >> 3, rem = nitems & 7;
+    Sched s;
+    s.first = x * per + imin(x, rem);
+    s.count = per + (x < rem ? 1 : 0);
+    s.K = (grid >> 3) + (x < (grid & 7) ? 1 : 0);
+    s.k = bid >> 3;
+    return s;
+}
+__host__ __device__ inline int sched_iters(const Sched& s) { return (s.count + s.K - 1) / s.K; }
+// Logical item of iteration it, or -1 (the last block may be partial).
+__host__ __device__ inline int sched_item(const Sched& s, int it) {
+    const int slot = it * s.K + ((it & 1) ? s.K - 1 - s.k : s.k);
+    return slot < s.count ? s.first + slot : -1;
+}
+// Workgroups of a launch over nitems items with at most `resident` of them
+// on the device at once.
+__host__ __device__ inline int sched_grid(int nitems, int resident) {
+    const int g = resident < 8 ? 8 : resident;
+    return nitems < g ? nitems : g;
 }
 
 // Key tiles a workgroup visits, and those a wave needs (causal: the wave's

@@ -6,11 +6,15 @@
 // fragments, staged K/V tile rows for the whole pipeline schedule including
 // the tiles prefetched past the end, scale indices, output columns and the
 // score-dump indices) and checks that it lies inside its buffer.  It also
-// checks that the block renumbering is a bijection.  Exit status 0 = clean.
+// checks that the work schedule visits every (batch, head, query tile) item
+// exactly once, for one item per workgroup and for the two-items-per-
+// workgroup grid of causal launches.  Exit status 0 = clean.
 #include "fwd_geometry.h"
 
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
+#include <utility>
 #include <vector>
 
 using namespace attn::geom;
@@ -43,17 +47,40 @@ static void check_shape(int B, int Hq, int S, bool causal, bool dump, int tile_l
     const size_t qk_head_bytes = static_cast<size_t>(S) * St::KROWG;
     const size_t v_head_bytes = static_cast<size_t>(S) * St::VROWG;
     const int nqblk = (S + 127) / 128, nkblk = (S + 63) / 64;
+    // the kernel's item loop: one item per workgroup, or (causal, no dump)
+    // the schedule over the two-items-per-workgroup grid as well
+    const bool persist = causal && !dump;
+    const int n = static_cast<int>(nblk);
+    std::vector<std::pair<int, int>> work;   // (grid, item) in visiting order
     std::vector<char> seen(nblk, 0);
-    for (long bid = 0; bid < nblk; ++bid) {
-        const BlockCoord c = decode_block(static_cast<int>(bid), static_cast<int>(nblk), Hq, ntiles,
-                                          tile_lo, causal && !dump);
+    for (int pass = 0; pass < (persist ? 2 : 1); ++pass) {
+        const int grid = pass == 0 ? n : sched_grid(n, (n + 1) / 2);
+        std::fill(seen.begin(), seen.end(), 0);
+        for (int bid = 0; bid < grid; ++bid) {
+            const Sched sc = make_sched(bid, grid, n);
+            const int iters = persist ? sched_iters(sc) : 1;
+            for (int it = 0; it < iters; ++it) {
+                const int item = sched_item(sc, it);
+                if (item < 0) continue;
+                REQUIRE(item < n && !seen[item], "grid %d bid %d it %d -> item %d", grid, bid, it, item);
+                if (item >= n || seen[item]) continue;
+                seen[item] = 1;
+                if (pass == 0) work.push_back({grid, item});
+            }
+        }
+        for (long i = 0; i < nblk; ++i) REQUIRE(seen[i], "grid %d: item %ld never visited", grid, i);
+    }
+    std::fill(seen.begin(), seen.end(), 0);
+    for (const auto& w : work) {
+        const int item = w.second;
+        const BlockCoord c = decode_item(item, Hq, ntiles, tile_lo, causal && !dump);
         REQUIRE(c.b >= 0 && c.b < B && c.pos >= 0 && c.pos < Hq && c.qt >= tile_lo &&
                     c.qt < tile_lo + ntiles && c.qt < nqt,
-                "bid %ld -> b %d pos %d qt %d", bid, c.b, c.pos, c.qt);
+                "item %d -> b %d pos %d qt %d", item, c.b, c.pos, c.qt);
         if (!(c.b >= 0 && c.b < B && c.pos >= 0 && c.pos < Hq && c.qt >= tile_lo && c.qt < tile_lo + ntiles))
             continue;
         const long slot = (static_cast<long>(c.b) * Hq + c.pos) * ntiles + (c.qt - tile_lo);
-        REQUIRE(!seen[slot], "bid %ld maps to a taken slot", bid);
+        REQUIRE(!seen[slot], "item %d maps to a taken slot", item);
         seen[slot] = 1;
         if (!all_heads && !((c.b == 0 && c.pos == 0) || (c.b == B - 1 && c.pos == Hq - 1))) continue;
 
@@ -269,9 +296,46 @@ static void check_mask_lists() {
     }
 }
 
+// The work schedule alone: for every item count up to 3000 and every grid
+// the launch may choose (one item per workgroup, two per workgroup, and any
+// grid between min(8, n) and n), each item is visited exactly once.
+static void check_schedules() {
+    std::vector<int> hits;
+    for (int n = 1; n <= 3000; ++n) {
+        const int lo = n < 8 ? n : 8;
+        std::vector<int> grids{n, sched_grid(n, (n + 1) / 2), sched_grid(n, (n + 2) / 3), sched_grid(n, 1), lo};
+        if (n <= 200)
+            for (int g = lo; g <= n; ++g) grids.push_back(g);
+        for (int grid : grids) {
+            REQUIRE(grid >= lo && grid <= n, "n %d grid %d", n, grid);
+            hits.assign(n, 0);
+            for (int bid = 0; bid < grid; ++bid) {
+                const Sched sc = make_sched(bid, grid, n);
+                REQUIRE(sc.K >= 1 && sc.k < sc.K, "n %d grid %d bid %d: k %d of %d", n, grid, bid, sc.k, sc.K);
+                for (int it = 0; it < sched_iters(sc); ++it) {
+                    const int item = sched_item(sc, it);
+                    if (item < 0) continue;
+                    REQUIRE(item >= sc.first && item < sc.first + sc.count, "item %d outside its XCD range", item);
+                    if (item >= 0 && item < n) hits[item] += 1;
+                }
+            }
+            for (int i = 0; i < n; ++i) REQUIRE(hits[i] == 1, "n %d grid %d: item %d visited %d times", n, grid, i, hits[i]);
+        }
+    }
+    // one item per workgroup keeps the plain XCD renumbering
+    for (int n = 1; n <= 600; ++n)
+        for (int bid = 0; bid < n; ++bid) {
+            const Sched sc = make_sched(bid, n, n);
+            const int x = bid & 7, per = n >> 3, rem = n & 7;
+            REQUIRE(sched_iters(sc) == 1 && sched_item(sc, 0) == x * per + imin(x, rem) + (bid >> 3),
+                    "n %d bid %d", n, bid);
+        }
+}
+
 int main() {
     long shapes = 0;
     check_mask_lists();
+    check_schedules();
     for (int S = 1; S <= 300; ++S) {
         check_all_paths<64>(1, 3, S, true);
         check_all_paths<128>(2, 2, S, true);

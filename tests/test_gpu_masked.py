@@ -157,3 +157,37 @@ def test_apb_mask_long_lists(S):
     rows = np.r_[0, anchor - 1, anchor + passing, S // 2, S - 1]
     exact = O.attention(q, k, v, causal=True, rows=rows)
     assert np.abs(host(o16).astype(np.float64)[:, :, rows] - exact).max() <= FP16_MAX_ABS
+
+
+@pytest.mark.parametrize("S,D,Hq,Hkv", [(1024, 128, 16, 4), (1000, 64, 20, 5)])
+def test_two_items_per_workgroup_is_bitwise_the_one_item_kernel(S, D, Hq, Hkv):
+    """Causal launches with at least 8 (batch, head, query tile) items per
+    compute unit run two items per workgroup (snake schedule); the tile-mask
+    kernel, which keeps one item per workgroup, computes the same tiles in
+    the same order, so the outputs and lse must agree bit for bit.  The batch
+    is sized from the device's compute-unit count so that the two-item path is
+    the one taken; the item count is not a multiple of 8 either."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nqt = (S + 127) // 128
+    B = (8 * cus) // (Hq * nqt) + 1
+    items = B * Hq * nqt
+    assert items >= 8 * cus
+    w = small_workload(B, Hq, Hkv, S, D, True, 900 + S)
+    q, k, v = make_qkv(w)
+    csr = A.block_mask_csr(S, _causal_mask(S))
+    case(f"two items per workgroup: B={B} Hq={Hq} S={S} D={D} items={items} cus={cus}")
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    c16, cl16 = A.fwd_fp16(qd, kd, vd, causal=True, return_lse=True)
+    m16, ml16 = A.fwd_fp16_masked(qd, kd, vd, csr, return_lse=True)
+    qz = A.quantize_qk(qd, kd)
+    c8, cl8 = A.fwd_int8(qz, vd, causal=True, return_lse=True)
+    m8, ml8 = A.fwd_int8_masked(qz, vd, csr, return_lse=True)
+    f8 = A.fwd_int8_fused_q(qd, A.quantize_k(kd), vd, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(c16, m16) and torch.equal(cl16, ml16)
+    assert torch.equal(c8, m8) and torch.equal(cl8, ml8)
+    assert torch.equal(f8, c8)
+    # and a sampled check against the oracle (rows of the first and last head)
+    rows = np.r_[0:3, S // 2, S - 1]
+    exact = O.attention(q[:1, :1], k[:1, :1], v[:1, :1], causal=True, rows=rows)
+    assert np.abs(host(c16)[:1, :1, rows].astype(np.float64) - exact).max() <= FP16_MAX_ABS
