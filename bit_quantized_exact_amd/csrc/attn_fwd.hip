@@ -72,6 +72,7 @@ typedef float f16x __attribute__((ext_vector_type(16)));
 typedef int i16x __attribute__((ext_vector_type(16)));
 typedef int i4x __attribute__((ext_vector_type(4)));
 typedef int i8x __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef __fp16 tr4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
 typedef __attribute__((address_space(3))) tr4 lds_tr4;
 
@@ -492,19 +493,26 @@ void fwd_kernel(const FwdParams p_in) {
         // leaves the maximum unchanged.
         const char* qrow = static_cast<const char*>(p.q) +
                            (bhq * S + static_cast<size_t>(geom::q_row(qi, S))) * (2 * D);
-        float xq[C::QSTEPS][16];
-        float amax = 0.0f;
+        h8 qraw[C::QSTEPS][2];
+#pragma unroll
+        for (int s = 0; s < C::QSTEPS; ++s)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) qraw[s][hh] = *reinterpret_cast<const h8*>(qrow + C::q16_piece_offset(s, g, hh));
+        // |x| max on the fp16 bit patterns: with the sign bit cleared, the
+        // integer order of finite values' patterns is the order of their
+        // magnitudes (two per 32-bit word, packed 16-bit maxima)
+        u16x2 mx2 = {0, 0};
 #pragma unroll
         for (int s = 0; s < C::QSTEPS; ++s)
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
-                const h8 v = *reinterpret_cast<const h8*>(qrow + C::q16_piece_offset(s, g, hh));
+                const i4x w = __builtin_bit_cast(i4x, qraw[s][hh]);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    xq[s][hh * 8 + e] = static_cast<float>(v[e]);
-                    amax = __builtin_fmaxf(amax, __builtin_fabsf(xq[s][hh * 8 + e]));
-                }
+                for (int e = 0; e < 4; ++e)
+                    mx2 = __builtin_elementwise_max(mx2, __builtin_bit_cast(u16x2, static_cast<unsigned>(w[e]) & 0x7fff7fffu));
             }
+        const unsigned short mx = mx2[0] > mx2[1] ? mx2[0] : mx2[1];
+        float amax = static_cast<float>(__builtin_bit_cast(_Float16, mx));
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, off));
         __shared__ float qmax[4];
@@ -513,19 +521,25 @@ void fwd_kernel(const FwdParams p_in) {
         const float a = __builtin_fmaxf(__builtin_fmaxf(qmax[0], qmax[1]), __builtin_fmaxf(qmax[2], qmax[3]));
         const float r = a == 0.0f ? 0.0f : __fdiv_rn(127.0f, a);
         qscale_fused = a == 0.0f ? 0.0f : __fdiv_rn(a, 127.0f);
+        // q = rint(x * r): |x * r| <= 127 (1 + 2^-23) here, so the clamp to
+        // [-127, 127] never acts, and adding 1.5 * 2^23 rounds x * r to an
+        // integer (nearest, ties to even, as rint) whose two's-complement low
+        // byte is the code.  (Product and sum rounded separately: no FMA.)
 #pragma unroll
         for (int s = 0; s < C::QSTEPS; ++s) {
             uint32_t w[4];
 #pragma unroll
             for (int e4 = 0; e4 < 4; ++e4) {
-                uint32_t packed = 0;
+                uint32_t b[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    float t = __builtin_rintf(xq[s][e4 * 4 + e] * r);
-                    t = __builtin_fminf(__builtin_fmaxf(t, -127.0f), 127.0f);
-                    packed |= (static_cast<uint32_t>(static_cast<int>(t)) & 0xffu) << (8 * e);
+#pragma clang fp contract(off)
+                    const float t = static_cast<float>(qraw[s][e4 >> 1][(e4 & 1) * 4 + e]) * r;
+                    b[e] = __float_as_uint(t + 12582912.0f);
                 }
-                w[e4] = packed;
+                const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);
+                const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u);
+                w[e4] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
             }
             __builtin_memcpy(&qf[s], w, 16);
         }
