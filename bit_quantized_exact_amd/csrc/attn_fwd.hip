@@ -1,5 +1,5 @@
-// Fused attention forward for gfx950: tiled, online softmax, one workgroup per
-// (batch, q-head, 128-row query tile).
+// Fused attention forward for gfx950: tiled, online softmax; the work items
+// are (batch, q-head, 128-row query tile), one or two per workgroup.
 //
 // What is computed (cited by page title and section):
 //   "注意力即一切：从 MHA 到 GQA" §2.2: scores Q K^T, softmax of the scaled
@@ -50,10 +50,14 @@
 //   * Branch-free tails: K/V rows beyond the sequence are loaded from the
 //     last row (clamped index) and masked to -inf, so no load is predicated.
 //   * Workgroups are launched XCD-aware: consecutive hardware block ids go
-//     round-robin over the 8 XCDs, so blocks are renumbered such that each
+//     round-robin over the 8 XCDs, so work items are numbered such that each
 //     XCD receives a contiguous range of (batch, head) pairs ordered by kv
 //     head; the q-heads of one GQA group then share K/V in that XCD's L2.
-//     Causal launches start with the heaviest (last) query tiles.
+//     Causal launches start with the heaviest (last) query tiles, and with
+//     many items they give each workgroup two (a heavy and a light one, in
+//     the snake order of geom::make_sched): the workgroups then carry equal
+//     work, and the in-order dispatch over the XCDs no longer stalls on an
+//     XCD whose slots are still busy.
 #include "attn_internal.h"
 #include "fwd_geometry.h"
 
