@@ -25,7 +25,8 @@ int check_shape(const attn_shape* s) {
     if (s->head_dim != 64 && s->head_dim != 128) return ATTN_EUNSUPPORTED;
     if (s->heads_q > ATTN_MAX_HEADS || s->heads_kv > ATTN_MAX_HEADS) return ATTN_EUNSUPPORTED;
     if (s->seq > ATTN_MAX_SEQ) return ATTN_EUNSUPPORTED;
-    // one workgroup per (batch, q-head, 128-row tile) must fit a 1-D grid
+    // the (batch, q-head, 128-row tile) work items are counted in an int and
+    // launched on a 1-D grid (one or two per workgroup)
     const long long blocks = static_cast<long long>(s->batch) * s->heads_q * ceil_div(s->seq, kBM);
     if (blocks > 0x7fffffffLL) return ATTN_EUNSUPPORTED;
     // the quantisation grids put batch*heads_kv (and batch) in grid dimension y/z
