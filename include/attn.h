@@ -28,7 +28,9 @@
  *   one sequence length.  head_dim must be 64 or 128.
  * Memory.  Every tensor pointer is DEVICE memory owned by the caller, 16-byte
  *   aligned.  The library allocates and frees nothing and keeps no mutable
- *   global state; calls are thread-safe.  kv_head_map is a HOST pointer.
+ *   global state beyond a per-device cache of the compute-unit count (which
+ *   sizes the forward launches); calls are thread-safe.  kv_head_map is a
+ *   HOST pointer.
  * Execution.  Every call enqueues its kernels on `stream` (a hipStream_t; NULL
  *   means the null stream) and returns without synchronising.
  * Errors.  Calls return a status code and never throw.  All argument checks run
