@@ -25,9 +25,11 @@ INT8 path attn_quantize_qk + attn_fwd_int8 are reported beside it, each as
 TFLOPS and as a fraction of MI355X's published dense MFMA peak (fp16
 2.5 PFLOP/s, int8 5.0 POP/s).
 
-`roofline` describes the dominant kernel of the step; `cpu_baseline` times the
-CPU oracle (fp64, plain loops) on a bounded sample of the same workload's
-query rows, on this machine's host cores.
+`roofline` describes the dominant kernel of the step; `mfma_loop` gives, as
+context for its published peak, the rate a dense MFMA loop sustains on this
+device (attn_probe_mfma); `cpu_baseline` times the CPU oracle (fp64, plain
+loops) on a bounded sample of the same workload's query rows, on this
+machine's host cores.
 
 Each timed section is preceded by untimed calls for CLOCK_WARM_MS of busy
 time (the clocks ramp up after the GPU idled while the CPU drew the inputs),
@@ -310,10 +312,70 @@ def run_workload(name, steps, warmup, cpu=False, cpu_seconds=15.0):
     rec["paths"]["decode"] = run_decode()
     if name == DEFAULT_WORKLOAD:
         rec["paths"]["apb_masked"] = run_apb(qd, kd, vd, qz, w)
+        rec["mfma_loop"] = run_mfma_loop()
     if cpu:
         rec["cpu_baseline"], rec["parity_sample"] = cpu_baseline(w, q, k, v, o8, o16, cpu_seconds,
                                                                  extra={"fp8_qk": of8, "int8_pv8": opv8})
     return rec
+
+
+def run_mfma_loop(iters=20000, reps=5):
+    """Sustained matrix-core rate of this device: a dense MFMA loop (four
+    independent accumulator chains per wave, two waves per SIMD on every
+    compute unit; attn_probe_mfma), timed with HIP events on the launch stream
+    after a clock warm-up.  Context for `roofline`, whose peak stays the
+    published figure.  `softmax_mix` times the FP16 loop with softmax-like
+    vector work beside every MFMA (one exp2 and five FMAs on independent
+    registers), that vector work alone, and both together: `hidden_frac` is
+    the share of the shorter of the two that runs under the other."""
+    import ctypes
+
+    import torch
+
+    import bit_quantized_exact_amd as A
+
+    L = A.lib()
+    cus = ctypes.c_int(0)
+    if L.attn_probe_compute_units(ctypes.byref(cus)) != 0 or cus.value <= 0:
+        return None
+    blocks = 2 * cus.value
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def time_kind(kind):
+        ops = ctypes.c_double(0.0)
+
+        def launch():
+            st = L.attn_probe_mfma(kind, blocks, iters, ctypes.c_void_p(sink.data_ptr()), ctypes.byref(ops),
+                                   ctypes.c_void_p(stream.cuda_stream))
+            if st != 0:
+                raise RuntimeError(f"attn_probe_mfma failed: {st}")
+
+        clock_warm(launch, min_ms=100, batch=2)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            launch()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps, ops.value
+
+    out = {"compute_units": cus.value, "waves_per_simd": 2}
+    ms = {}
+    for kind, key, fkey, peak in ((0, "fp16_tflops", "fp16_frac_of_published_peak", PEAK_TFLOPS["fp16"]),
+                                  (1, "int8_tops", "int8_frac_of_published_peak", PEAK_TFLOPS["int8"])):
+        t, ops = time_kind(kind)
+        ms[kind] = t
+        rate = ops / (t * 1e-3) / 1e12
+        out[key] = round(rate, 1)
+        out[fkey] = round(rate / peak, 4)
+    t_both, _ = time_kind(2)
+    t_valu, _ = time_kind(3)
+    t_mfma = ms[0]
+    out["softmax_mix"] = {"mfma_alone_ms": round(t_mfma, 4), "valu_alone_ms": round(t_valu, 4),
+                          "both_ms": round(t_both, 4),
+                          "hidden_frac": round((t_mfma + t_valu - t_both) / min(t_mfma, t_valu), 3)}
+    return out
 
 
 def run_decode(name="decode_gqa", reps=20, warm_ms=None):

@@ -25,6 +25,7 @@ EXPORTED = (
     "attn_quantize_v_fp8", "attn_fwd_int8_pv8", "attn_decode_workspace_bytes", "attn_decode_int8",
     "attn_decode_fp16", "attn_block_mask_tiles", "attn_block_mask_apb", "attn_block_mask_csr",
     "attn_fwd_fp16_masked", "attn_fwd_int8_masked",
+    "attn_probe_mfma", "attn_probe_compute_units",
 )
 
 
@@ -102,5 +103,9 @@ def lib():
     L.attn_fwd_int8_masked.restype = ctypes.c_int
     L.attn_status_string.argtypes = [ctypes.c_int]
     L.attn_status_string.restype = ctypes.c_char_p
+    L.attn_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, ctypes.POINTER(ctypes.c_double), P]
+    L.attn_probe_mfma.restype = ctypes.c_int
+    L.attn_probe_compute_units.argtypes = [ctypes.POINTER(ctypes.c_int)]
+    L.attn_probe_compute_units.restype = ctypes.c_int
     _lib = L
     return L

@@ -29,6 +29,7 @@ SOURCES = {
     "attn_fwd.hip": [],
     "attn_decode.hip": [],
     "attn_api.hip": [],
+    "mfma_probe.hip": [],
 }
 
 

@@ -1,6 +1,7 @@
 """C-ABI checks that need no GPU: the library loads, exports every symbol that
-include/attn.h declares, and rejects every invalid argument on the host,
-before any HIP call (each call below fails validation, so nothing launches)."""
+include/attn.h and include/attn_probe.h declare, and rejects every invalid
+argument on the host, before any HIP call (each call below fails validation,
+so nothing launches)."""
 import ctypes
 import os
 import re
@@ -16,9 +17,12 @@ MISALIGNED = 0x10008
 
 
 def _declared():
-    text = open(os.path.join(ROOT, "include", "attn.h")).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in ("attn.h", "attn_probe.h"):
+        text = open(os.path.join(ROOT, "include", h)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_and_binding_agree():
@@ -306,3 +310,14 @@ def test_decode_workspace_and_validation():
     odd = _kv(Hq=6, Hkv=4)
     assert L.attn_decode_fp16(ctypes.byref(odd), FAKE, FAKE, FAKE, FAKE, None, None, 1, 0.0, FAKE,
                               None) == -1
+
+
+def test_mfma_probe_rejects_bad_arguments():
+    L = A.lib()
+    ops = ctypes.c_double(0.0)
+    assert L.attn_probe_mfma(4, 1, 1, FAKE, ctypes.byref(ops), None) == -1    # unknown kind
+    assert L.attn_probe_mfma(-1, 1, 1, FAKE, ctypes.byref(ops), None) == -1   # unknown kind
+    assert L.attn_probe_mfma(0, 0, 1, FAKE, ctypes.byref(ops), None) == -1    # no blocks
+    assert L.attn_probe_mfma(1, 1, 0, FAKE, ctypes.byref(ops), None) == -1    # no iterations
+    assert L.attn_probe_mfma(0, 1, 1, None, ctypes.byref(ops), None) == -1    # no sink
+    assert L.attn_probe_compute_units(None) == -1
