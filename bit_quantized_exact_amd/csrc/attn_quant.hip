@@ -19,8 +19,10 @@
 //     divisions, one product, rint) are single IEEE operations.  This file is
 //     compiled with -ffp-contract=off so that no product is fused.
 //
-// All four kernels stream HBM: each reads its inputs once (K twice: sums, then
-// quantisation) with 16-byte loads and writes int8 with 8-byte stores.
+// The kernels stream HBM: each reads its inputs once (K twice: sums, then
+// quantisation) with 16-byte loads and writes int8 with 8-byte stores.  Up to
+// 8192 tokens the K quantiser adds the chunk sums of its (b, kv-head) itself,
+// so K takes two launches (sums, quantisation) instead of three.
 #include "attn_internal.h"
 
 #include <cfloat>
@@ -153,12 +155,19 @@ __device__ __forceinline__ unsigned e4m3_pair(float x0, float x1, float r) {
 // SMOOTH subtracts the channel mean first (K); Q is quantised as is.  FP8
 // selects the E4M3 grid (448 in place of 127, E4M3 rounding in place of
 // rint + clamp): the FP8 alternative the SageAttention article compares with.
-template <int D, int ROWS, bool SMOOTH, bool FP8 = false>
+// MEANP (with SMOOTH): the workgroup adds the per-chunk exact channel sums of
+// its (b, kv-head) itself - the same integer totals and the same division as
+// k_mean_kernel, so the same means - instead of reading them from `mean`;
+// for short sequences this saves the separate mean launch.  The block with
+// blk == 0 writes the means to mean_out when it is not null.
+template <int D, int ROWS, bool SMOOTH, bool FP8 = false, bool MEANP = false>
 __global__ __launch_bounds__(256) void quant_block_kernel(const uint16_t* __restrict__ x,
                                                           const float* __restrict__ mean,
                                                           int8_t* __restrict__ q,
                                                           float* __restrict__ scale, int H,
-                                                          int S, int nblk) {
+                                                          int S, int nblk,
+                                                          const long long* __restrict__ partial,
+                                                          int nchunk, float* __restrict__ mean_out) {
     constexpr float kTop = FP8 ? 448.0f : 127.0f;
     constexpr int CPR = D / 8;
     constexpr int CHUNKS = ROWS * CPR;
@@ -174,8 +183,38 @@ __global__ __launch_bounds__(256) void quant_block_kernel(const uint16_t* __rest
     const int r0 = blk * ROWS;
 
     float mu[8];
+    if constexpr (MEANP) {
+        static_assert(SMOOTH && 256 % D == 0, "means from chunk sums: smoothed K");
+        constexpr int G = 256 / D;   // threads per channel
+        __shared__ long long red[G][D];
+        __shared__ float smu[D];
+        const int c = t % D, grp = t / D;
+        const long long* src = partial + mat * static_cast<size_t>(nchunk) * D + c;
+        long long s4[4] = {0, 0, 0, 0};
+        int i = grp;
+        for (; i + 3 * G < nchunk; i += 4 * G) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) mu[e] = SMOOTH ? mean[mat * D + cc * 8 + e] : 0.0f;
+            for (int u = 0; u < 4; ++u) s4[u] += src[static_cast<size_t>(i + u * G) * D];
+        }
+        for (; i < nchunk; i += G) s4[0] += src[static_cast<size_t>(i) * D];
+        red[grp][c] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+        __syncthreads();
+        if (grp == 0) {
+            long long tot = 0;
+#pragma unroll
+            for (int g2 = 0; g2 < G; ++g2) tot += red[g2][c];
+            const double total = __builtin_ldexp(static_cast<double>(tot), -24);
+            const float m = static_cast<float>(total / static_cast<double>(S));
+            smu[c] = m;
+            if (mean_out && blk == 0) mean_out[mat * D + c] = m;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mu[e] = smu[cc * 8 + e];
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mu[e] = SMOOTH ? mean[mat * D + cc * 8 + e] : 0.0f;
+    }
 
     float v[PER][8];
     float amax = 0.0f;
@@ -352,6 +391,11 @@ __global__ __launch_bounds__(256) void v_quant_kernel(const uint16_t* __restrict
     }
 }
 
+// Up to this many chunk sums per (b, kv-head) (sequences up to 8192 tokens)
+// the K quantiser adds them itself; longer sequences keep the mean kernel,
+// whose one reduction per (b, kv-head) is cheaper than one per K block.
+constexpr int kMeanInQuantMaxChunks = 32;
+
 template <int D, bool FP8>
 int launch_quantize_d(const attn_shape& s, const void* q, const void* k, int8_t* q_i8,
                       float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
@@ -362,15 +406,23 @@ int launch_quantize_d(const attn_shape& s, const void* q, const void* k, int8_t*
     const uint16_t* qq = static_cast<const uint16_t*>(q);
     hipLaunchKernelGGL(k_colsum_kernel<D>, dim3(ws.nchunk, BH_kv), dim3(kColsumThreads), 0, st, kk, S,
                        ws.nchunk, ws.partial);
-    hipLaunchKernelGGL(k_mean_kernel<D>, dim3(BH_kv), dim3(D * kMeanGroups), 0, st, ws.partial, S, ws.nchunk,
-                       ws.mean, k_mean);
     const int nkb = ceil_div(S, kBK), nqb = ceil_div(S, kBQ);
-    hipLaunchKernelGGL((quant_block_kernel<D, kBK, true, FP8>), dim3(nkb, s.heads_kv, s.batch),
-                       dim3(256), 0, st, kk, ws.mean, k_i8, k_scale, s.heads_kv, S, nkb);
+    if (ws.nchunk <= kMeanInQuantMaxChunks) {
+        hipLaunchKernelGGL((quant_block_kernel<D, kBK, true, FP8, true>), dim3(nkb, s.heads_kv, s.batch),
+                           dim3(256), 0, st, kk, static_cast<const float*>(nullptr), k_i8, k_scale, s.heads_kv,
+                           S, nkb, ws.partial, ws.nchunk, k_mean);
+    } else {
+        hipLaunchKernelGGL(k_mean_kernel<D>, dim3(BH_kv), dim3(D * kMeanGroups), 0, st, ws.partial, S, ws.nchunk,
+                           ws.mean, k_mean);
+        hipLaunchKernelGGL((quant_block_kernel<D, kBK, true, FP8>), dim3(nkb, s.heads_kv, s.batch),
+                           dim3(256), 0, st, kk, ws.mean, k_i8, k_scale, s.heads_kv, S, nkb,
+                           static_cast<const long long*>(nullptr), 0, static_cast<float*>(nullptr));
+    }
     if (qq)
         hipLaunchKernelGGL((quant_block_kernel<D, kBQ, false, FP8>), dim3(nqb, s.heads_q, s.batch),
                            dim3(256), 0, st, qq, static_cast<const float*>(nullptr), q_i8, q_scale,
-                           s.heads_q, S, nqb);
+                           s.heads_q, S, nqb, static_cast<const long long*>(nullptr), 0,
+                           static_cast<float*>(nullptr));
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ELAUNCH;
 }
 
