@@ -18,6 +18,8 @@ SMALL = [
     (2, 2, 2, 63, 64), (1, 2, 2, 64, 128), (1, 3, 3, 65, 64), (1, 4, 1, 127, 128),
     (1, 2, 2, 128, 64), (2, 4, 2, 129, 128), (1, 2, 2, 255, 64), (1, 2, 1, 257, 128),
     (1, 8, 2, 1000, 128), (3, 2, 2, 513, 64),
+    # 32 chunk sums (the K quantiser adds them itself) and 33 (the mean kernel runs)
+    (1, 2, 1, 8192, 64), (1, 2, 2, 8193, 128),
 ]
 
 
