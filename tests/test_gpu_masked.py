@@ -191,3 +191,36 @@ def test_two_items_per_workgroup_is_bitwise_the_one_item_kernel(S, D, Hq, Hkv):
     rows = np.r_[0:3, S // 2, S - 1]
     exact = O.attention(q[:1, :1], k[:1, :1], v[:1, :1], causal=True, rows=rows)
     assert np.abs(host(c16)[:1, :1, rows].astype(np.float64) - exact).max() <= FP16_MAX_ABS
+
+
+@pytest.mark.parametrize("S,D,Hq,Hkv,kv_map", [(700, 128, 8, 2, None), (1024, 64, 12, 3, [2, 0, 1] * 4)])
+def test_results_do_not_depend_on_the_launch_size(S, D, Hq, Hkv, kv_map):
+    """A batch large enough for two items per workgroup gives, for its first
+    and last sequence, bit for bit what a launch of that sequence alone (one
+    item per workgroup) gives: FP16, two-call INT8 and fused INT8 forwards,
+    outputs and lse, under an explicit kv-head map too."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nqt = (S + 127) // 128
+    B = (8 * cus) // (Hq * nqt) + 2
+    w = small_workload(B, Hq, Hkv, S, D, True, 950 + S)
+    q, k, v = make_qkv(w)
+    case(f"launch-size invariance: B={B} Hq={Hq} Hkv={Hkv} S={S} D={D} map={kv_map} cus={cus}")
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    kz = A.quantize_k(kd)
+    qz = A.quantize_qk(qd, kd)
+
+    def run(sl):
+        qs, ks, vs = qd[sl].contiguous(), kd[sl].contiguous(), vd[sl].contiguous()
+        kzs = {key: (t[sl].contiguous() if isinstance(t, torch.Tensor) and t.dim() > 1 else t) for key, t in kz.items()}
+        qzs = {key: (t[sl].contiguous() if isinstance(t, torch.Tensor) and t.dim() > 1 else t) for key, t in qz.items()}
+        o16, l16 = A.fwd_fp16(qs, ks, vs, causal=True, kv_head_map=kv_map, return_lse=True)
+        o8, l8 = A.fwd_int8(qzs, vs, causal=True, kv_head_map=kv_map, return_lse=True)
+        f8, fl8 = A.fwd_int8_fused_q(qs, kzs, vs, causal=True, kv_head_map=kv_map, return_lse=True)
+        return [o16, l16, o8, l8, f8, fl8]
+
+    full = run(slice(0, B))
+    for b in (0, B - 1):
+        one = run(slice(b, b + 1))
+        torch.cuda.synchronize()
+        for x, y in zip(full, one):
+            assert torch.equal(x[b:b + 1], y)
