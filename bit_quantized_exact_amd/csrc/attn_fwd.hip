@@ -455,10 +455,13 @@ void fwd_kernel(const FwdParams p_in) {
     };
     float ksring[3] = {1.0f, 1.0f, 1.0f};
 
-    // The first K tile's loads are issued before Q is read and quantised,
-    // so the two latencies overlap (direct-to-LDS: the whole prologue's
-    // copies, K_0 .. K_{NST-1} and V_0 .. V_{NST-2}).
-    if constexpr (DTL) {
+    // The prologue's copies into LDS (K_0 .. K_{NST-1}, V_0 .. V_{NST-2})
+    // and Q's loads overlap.  The INT8 kernels issue the copies first (and
+    // the first K scales after them); the FP16 kernels load Q first, so that
+    // the first score tile waits for Q and K_0 only, not for the whole copy
+    // queue.  (Register staging: K_0's loads go out before Q.)
+    constexpr bool QFIRST = DTL && !INT8;
+    auto dtl_prologue = [&]() __attribute__((always_inline)) {
         dtl_k(tile_row(0), dks[0]);
         dtl_k(tile_row(1), dks[1]);
         dtl_v(tile_row(0), dvs[0]);
@@ -466,11 +469,14 @@ void fwd_kernel(const FwdParams p_in) {
             dtl_k(tile_row(2), dks[2]);
             dtl_v(tile_row(1), dvs[1]);
         }
+    };
+    if constexpr (DTL && !QFIRST) {
+        dtl_prologue();
         if constexpr (INT8) {
 #pragma unroll
             for (int t = 0; t < NST; ++t) ksring[t] = kscale_at(t);
         }
-    } else if constexpr (!DUMP) {
+    } else if constexpr (!DTL && !DUMP) {
         gload_k(tile_row(0), kreg[0]);
     }
 
@@ -486,6 +492,7 @@ void fwd_kernel(const FwdParams p_in) {
             // 16 bytes per lane: int8 elements s*32 + g*16.., or fp16 elements s*16 + g*8..
             qf[s] = *reinterpret_cast<const qfrag_t*>(qrow + C::q_frag_offset(s, g));
         }
+        if constexpr (QFIRST) dtl_prologue();
     } else {
         // In-kernel per-block quantisation of Q (SageAttention article,
         // 技术方案: INT8 Q with one scale per FlashAttention-sized block).  The
@@ -591,7 +598,8 @@ void fwd_kernel(const FwdParams p_in) {
         constexpr bool kBiased = INT8 && !F8;   // INT32 scores read as biased fp32
         acc_t sc[2];
         if constexpr (DTL) {
-            lds_stage_barrier<0>();   // every prologue copy has landed
+            // every prologue copy has landed (FP16: K_0; the later copies may be in flight)
+            lds_stage_barrier<QFIRST ? (NST == 3 ? 2 * DK::NI + 2 * VNI : DK::NI + VNI) : 0>();
             score_tile<D, INT8, F8, kBiased, true>(dks[0], qf, l32, g, sc);
         } else {
             sstore_k(0, kreg[0]);
