@@ -157,6 +157,22 @@ __device__ __forceinline__ void lds_stage_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// One direct-to-LDS copy: 16 bytes per lane from base + off into the LDS
+// block at lds + 16 * lane (global_load_lds_dwordx4, saddr form).  Issued as
+// inline asm: issued with the builtin, the compiler's wait counting treats
+// every LDS read as unordered while such a copy is in flight and drains all
+// LDS reads (lgkmcnt(0)) wherever it waits for one; the copies' completion is
+// tracked by the explicit waits of lds_stage_barrier in any case.  s_nop 4
+// covers the wait states after a vector instruction that wrote an SGPR the
+// copy reads (the hazard recognizer does not look at asm inputs), s_nop 0 the
+// M0 write before an LDS DMA.
+__device__ __forceinline__ void dtl_copy16(const char* base, uint32_t off, const char* lds) {
+    const uint32_t m0v = static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)lds));
+    asm volatile("s_nop 4\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(off), "s"(base), "s"(m0v) : "memory", "m0");
+}
+
 #ifndef ATTN_FWD_DTL
 #define ATTN_FWD_DTL 1
 #endif
@@ -412,9 +428,7 @@ void fwd_kernel(const FwdParams p_in) {
             const int r = DK::slot_row(wave, i, lane);
             const int c = DK::slot_chunk(wave, i, lane) ^ DK::k_swz(r);
             const uint32_t off = static_cast<uint32_t>(geom::tile_lane_row(r, first, S)) * C::KROWG + c * 16;
-            __builtin_amdgcn_global_load_lds(base + off,
-                                             (__attribute__((address_space(3))) void*)(st + (wave_s * DK::NI + i) * 1024),
-                                             16, 0, 0);
+            dtl_copy16(base, off, st + (wave_s * DK::NI + i) * 1024);
         }
     };
     using D8 = geom::Dtl8<D>;
@@ -428,9 +442,7 @@ void fwd_kernel(const FwdParams p_in) {
                 const int r = D8::slot_row(wave, i, lane);
                 const int c = D8::slot_chunk(wave, i, lane) ^ D8::swz(r);
                 const uint32_t off = static_cast<uint32_t>(r) * vt_stride + c * 16;
-                __builtin_amdgcn_global_load_lds(base + off,
-                                                 (__attribute__((address_space(3))) void*)(st + (wave_s * D8::NI + i) * 1024),
-                                                 16, 0, 0);
+                dtl_copy16(base, off, st + (wave_s * D8::NI + i) * 1024);
             }
             return;
         }
@@ -441,9 +453,7 @@ void fwd_kernel(const FwdParams p_in) {
             const int r = DV::slot_row(wave, i, lane);
             const int c = DV::slot_chunk(wave, i, lane) ^ DV::v_swz(r);
             const uint32_t off = static_cast<uint32_t>(geom::tile_lane_row(r, first, S)) * C::VROWG + c * 16;
-            __builtin_amdgcn_global_load_lds(base + off,
-                                             (__attribute__((address_space(3))) void*)(st + (wave_s * DV::NI + i) * 1024),
-                                             16, 0, 0);
+            dtl_copy16(base, off, st + (wave_s * DV::NI + i) * 1024);
         }
     };
     char* dks[3] = {dk0, dk1, dk2};
