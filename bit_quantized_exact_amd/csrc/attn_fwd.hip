@@ -157,20 +157,42 @@ __device__ __forceinline__ void lds_stage_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// One direct-to-LDS copy: 16 bytes per lane from base + off into the LDS
-// block at lds + 16 * lane (global_load_lds_dwordx4, saddr form).  Issued as
-// inline asm: issued with the builtin, the compiler's wait counting treats
-// every LDS read as unordered while such a copy is in flight and drains all
-// LDS reads (lgkmcnt(0)) wherever it waits for one; the copies' completion is
-// tracked by the explicit waits of lds_stage_barrier in any case.  s_nop 4
+// Direct-to-LDS copies: 16 bytes per lane from base + off[i] into the LDS
+// block at lds + 1024 i + 16 * lane (global_load_lds_dwordx4, saddr form),
+// N of them in one inline-asm block.  Issued with the builtin, the
+// compiler's wait counting treats every LDS read as unordered while such a
+// copy is in flight and drains all LDS reads (lgkmcnt(0)) wherever it waits
+// for one; the copies' completion is tracked by the explicit waits of
+// lds_stage_barrier in any case.  The s_nop 4 at the head of the block
 // covers the wait states after a vector instruction that wrote an SGPR the
-// copy reads (the hazard recognizer does not look at asm inputs), s_nop 0 the
-// M0 write before an LDS DMA.
-__device__ __forceinline__ void dtl_copy16(const char* base, uint32_t off, const char* lds) {
-    const uint32_t m0v = static_cast<uint32_t>(
+// copies read (every input is written before the block; the hazard
+// recognizer does not look at asm inputs), each s_nop 0 the M0 write before
+// an LDS DMA.
+template <int N>
+__device__ __forceinline__ void dtl_copies(const char* base, const uint32_t (&off)[N], const char* lds) {
+    static_assert(N == 1 || N == 2 || N == 4, "copies per block");
+    const uint32_t l0 = static_cast<uint32_t>(
         reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)lds));
-    asm volatile("s_nop 4\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :: "v"(off), "s"(base), "s"(m0v) : "memory", "m0");
+    if constexpr (N == 1) {
+        asm volatile("s_nop 4\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                     :: "v"(off[0]), "s"(base), "s"(l0) : "memory", "m0");
+    } else if constexpr (N == 2) {
+        const uint32_t l1 = l0 + 1024;
+        asm volatile("s_nop 4\n\t"
+                     "s_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2\n\t"
+                     "s_mov_b32 m0, %4\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     :: "v"(off[0]), "v"(off[1]), "s"(base), "s"(l0), "s"(l1) : "memory", "m0");
+    } else {
+        const uint32_t l1 = l0 + 1024, l2 = l0 + 2048, l3 = l0 + 3072;
+        asm volatile("s_nop 4\n\t"
+                     "s_mov_b32 m0, %5\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %4\n\t"
+                     "s_mov_b32 m0, %6\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %4\n\t"
+                     "s_mov_b32 m0, %7\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %4\n\t"
+                     "s_mov_b32 m0, %8\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %3, %4"
+                     :: "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "s"(base), "s"(l0), "s"(l1),
+                        "s"(l2), "s"(l3)
+                     : "memory", "m0");
+    }
 }
 
 #ifndef ATTN_FWD_DTL
@@ -423,13 +445,14 @@ void fwd_kernel(const FwdParams p_in) {
     auto dtl_k = [&](int n0, char* st) __attribute__((always_inline)) {
         const int first = geom::tile_first_row(n0, S);
         const char* base = kg + static_cast<size_t>(first) * C::KROWG;
+        uint32_t off[DK::NI];
 #pragma unroll
         for (int i = 0; i < DK::NI; ++i) {
             const int r = DK::slot_row(wave, i, lane);
             const int c = DK::slot_chunk(wave, i, lane) ^ DK::k_swz(r);
-            const uint32_t off = static_cast<uint32_t>(geom::tile_lane_row(r, first, S)) * C::KROWG + c * 16;
-            dtl_copy16(base, off, st + (wave_s * DK::NI + i) * 1024);
+            off[i] = static_cast<uint32_t>(geom::tile_lane_row(r, first, S)) * C::KROWG + c * 16;
         }
+        dtl_copies<DK::NI>(base, off, st + wave_s * DK::NI * 1024);
     };
     using D8 = geom::Dtl8<D>;
     constexpr int VNI = PV8 ? D8::NI : DV::NI;   // V copy instructions per wave per tile
@@ -437,24 +460,26 @@ void fwd_kernel(const FwdParams p_in) {
         if constexpr (PV8) {
             // D rows of 64 key codes of the V^T tile at column v8_tile_col
             const char* base = vg + geom::v8_tile_col(n0, p.nkblk);
+            uint32_t off[D8::NI];
 #pragma unroll
             for (int i = 0; i < D8::NI; ++i) {
                 const int r = D8::slot_row(wave, i, lane);
                 const int c = D8::slot_chunk(wave, i, lane) ^ D8::swz(r);
-                const uint32_t off = static_cast<uint32_t>(r) * vt_stride + c * 16;
-                dtl_copy16(base, off, st + (wave_s * D8::NI + i) * 1024);
+                off[i] = static_cast<uint32_t>(r) * vt_stride + c * 16;
             }
+            dtl_copies<D8::NI>(base, off, st + wave_s * D8::NI * 1024);
             return;
         }
         const int first = geom::tile_first_row(n0, S);
         const char* base = vg + static_cast<size_t>(first) * C::VROWG;
+        uint32_t off[DV::NI];
 #pragma unroll
         for (int i = 0; i < DV::NI; ++i) {
             const int r = DV::slot_row(wave, i, lane);
             const int c = DV::slot_chunk(wave, i, lane) ^ DV::v_swz(r);
-            const uint32_t off = static_cast<uint32_t>(geom::tile_lane_row(r, first, S)) * C::VROWG + c * 16;
-            dtl_copy16(base, off, st + (wave_s * DV::NI + i) * 1024);
+            off[i] = static_cast<uint32_t>(geom::tile_lane_row(r, first, S)) * C::VROWG + c * 16;
         }
+        dtl_copies<DV::NI>(base, off, st + wave_s * DV::NI * 1024);
     };
     char* dks[3] = {dk0, dk1, dk2};
     char* dvs[3] = {dv0, dv1, dv2};
