@@ -328,6 +328,11 @@ void fwd_kernel(const FwdParams p_in) {
     const int l32 = lane & 31;
     const int g = lane >> 5;
     const int S = p.S;
+    // The softmax scale, read once per item into a register the compiler
+    // cannot re-derive: read through p inside the key loop it becomes a
+    // scalar load per tile whose wait (lgkmcnt) also drains the LDS reads.
+    float scale_log2 = p.scale_log2;
+    if constexpr (PERSIST) asm volatile("" : "+s"(scale_log2));
     // (tile masks are mostly causal-like too, heavier for later query tiles)
     const geom::BlockCoord bc = geom::decode_item(item, p.Hq, p.ntiles, p.tile_lo, (CAUSAL || BMASK) && !DUMP);
     const int b = bc.b;
@@ -666,8 +671,8 @@ void fwd_kernel(const FwdParams p_in) {
             const int n0 = tile_row(j);
             {
                 // scores in log2 units: s * c with c = (dQ dK) sm_scale log2(e)
-                float c = p.scale_log2;
-                if constexpr (INT8) c = fmaxf(qscale * kscale_j * p.scale_log2, FLT_MIN);
+                float c = scale_log2;
+                if constexpr (INT8) c = fmaxf(qscale * kscale_j * scale_log2, FLT_MIN);
                 float sv[2][16];
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt)
