@@ -447,9 +447,35 @@ void fwd_kernel(const FwdParams p_in) {
     using DK = geom::Dtl<C::KROWG>;
     using DV = geom::Dtl<2 * D>;
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    // Per-lane offsets of a whole tile (no row clamped), the same for every
+    // tile.  Made opaque so that the compiler keeps them as they are rather
+    // than folding them into the clamped form it computes per tile.  (Not in
+    // the one-item head_dim-64 kernels: there the extra registers spill.)
+    constexpr bool WHOLE = PERSIST || D == 128;
+    uint32_t koff_whole[DK::NI], voff_whole[DV::NI];
+    if constexpr (WHOLE) {
+#pragma unroll
+        for (int i = 0; i < DK::NI; ++i) {
+            const int r = DK::slot_row(wave, i, lane);
+            koff_whole[i] = static_cast<uint32_t>(r) * C::KROWG + (DK::slot_chunk(wave, i, lane) ^ DK::k_swz(r)) * 16;
+            asm volatile("" : "+v"(koff_whole[i]));
+        }
+#pragma unroll
+        for (int i = 0; i < DV::NI; ++i) {
+            const int r = DV::slot_row(wave, i, lane);
+            voff_whole[i] = static_cast<uint32_t>(r) * C::VROWG + (DV::slot_chunk(wave, i, lane) ^ DV::v_swz(r)) * 16;
+            asm volatile("" : "+v"(voff_whole[i]));
+        }
+    }
     auto dtl_k = [&](int n0, char* st) __attribute__((always_inline)) {
         const int first = geom::tile_first_row(n0, S);
         const char* base = kg + static_cast<size_t>(first) * C::KROWG;
+        // A whole tile (every row inside the sequence: all but the last)
+        // takes the unclamped offsets computed once per item.
+        if (WHOLE && n0 + kBN <= S) {
+            dtl_copies<DK::NI>(base, koff_whole, st + wave_s * DK::NI * 1024);
+            return;
+        }
         uint32_t off[DK::NI];
 #pragma unroll
         for (int i = 0; i < DK::NI; ++i) {
@@ -477,6 +503,10 @@ void fwd_kernel(const FwdParams p_in) {
         }
         const int first = geom::tile_first_row(n0, S);
         const char* base = vg + static_cast<size_t>(first) * C::VROWG;
+        if (WHOLE && n0 + kBN <= S) {   // (a whole tile, as for K)
+            dtl_copies<DV::NI>(base, voff_whole, st + wave_s * DV::NI * 1024);
+            return;
+        }
         uint32_t off[DV::NI];
 #pragma unroll
         for (int i = 0; i < DV::NI; ++i) {
