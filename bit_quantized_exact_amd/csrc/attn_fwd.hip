@@ -199,6 +199,30 @@ __device__ __forceinline__ void dtl_copies(const char* base, const uint32_t (&of
 #define ATTN_FWD_DTL 1
 #endif
 
+typedef const __attribute__((address_space(3))) char* lds_cptr;
+
+// FP16 scores of one 64-key tile as score_tile computes them (same MFMAs in
+// the same order), from per-lane LDS addresses of the K chunks the wave
+// reads at each k-step, given for query-row block 0 (block 1 lies 32 rows
+// further: the swizzle repeats every 32 rows at this row size).
+template <int D, int N, typename QF, typename ACC>
+__device__ __forceinline__ void score_tile_at(const lds_cptr (&ka)[N], const QF* qf, ACC* acc) {
+    using C = Cfg<D, false, false>;
+    static_assert(N == C::QSTEPS, "one address per k-step");
+    static_assert(32 % geom::Dtl<C::KROWG>::RPL == 0 && (32 / geom::Dtl<C::KROWG>::RPL) % geom::Dtl<C::KROWG>::CPR == 0,
+                  "the K swizzle must repeat every 32 rows");
+    typedef const __attribute__((address_space(3))) h8 lds_h8;
+    acc[0] = typename C::acc_t{};
+    acc[1] = typename C::acc_t{};
+#pragma unroll
+    for (int s = 0; s < C::QSTEPS; ++s)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            const h8 a = *(lds_h8*)(ka[s] + mt * 32 * C::KROWG);
+            acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[s], acc[mt], 0, 0, 0);
+        }
+}
+
 // Transposed scores of one 64-key tile for this wave's 32 queries:
 // acc[mt] holds keys mt*32 + (r/4)*8 + (lane/32)*4 + r%4 (register r) of query
 // lane%32.  The same code feeds the forward and the INT32 score dump.
@@ -518,6 +542,20 @@ void fwd_kernel(const FwdParams p_in) {
     };
     char* dks[3] = {dk0, dk1, dk2};
     char* dvs[3] = {dv0, dv1, dv2};
+    // FP16 head_dim 128 (two stages): the K read addresses of both stages,
+    // computed once per item and kept in registers (opaque to the compiler,
+    // which otherwise re-adds the stage base to each lane offset per tile).
+    constexpr bool KADDR = DTL && !INT8 && !F8 && D == 128 && NST == 2;
+    lds_cptr kaddr[2][C::QSTEPS];
+    if constexpr (KADDR) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int s = 0; s < C::QSTEPS; ++s) {
+                kaddr[st][s] = (lds_cptr)(dks[st] + l32 * C::KROWG + (((2 * s + g) ^ DK::k_swz(l32)) << 4));
+                asm volatile("" : "+v"(kaddr[st][s]));
+            }
+    }
     // K scale of key tile t (clamped to the last block; tiles past the end are never used)
     auto kscale_at = [&](int t) -> float {
         if constexpr (BMASK) t = tile_row(t) / kBN;   // (list position -> key tile)
@@ -695,7 +733,7 @@ void fwd_kernel(const FwdParams p_in) {
         // One key tile: the softmax of S_j, the scores S_{j+1} from the K tile
         // at ksn and O^T += V_j^T P_j^T from the V tile at vsc (padded rows,
         // or the swizzled unpadded rows of direct-to-LDS staging when SWZ).
-        auto compute = [&](int j, const char* ksn, const char* vsc, float kscale_j, auto swz_tag)
+        auto compute = [&](int j, const char* ksn, int kst, const char* vsc, float kscale_j, auto swz_tag)
                            __attribute__((always_inline)) {
             constexpr bool SWZ = decltype(swz_tag)::value;
             const int n0 = tile_row(j);
@@ -754,7 +792,8 @@ void fwd_kernel(const FwdParams p_in) {
                 // row maxima (same-run A/B: +3-4 % on the 8192-token prefill).
                 __builtin_amdgcn_s_setprio(1);
                 acc_t sn[2];
-                score_tile<D, INT8, F8, kBiased, SWZ>(ksn, qf, l32, g, sn);
+                if constexpr (KADDR && SWZ) score_tile_at<D>(kaddr[kst], qf, sn);
+                else score_tile<D, INT8, F8, kBiased, SWZ>(ksn, qf, l32, g, sn);
 
                 const float m_eff = BMASK && m_run == -INFINITY ? 0.0f : m_run;   // (masked rows: weights 0)
                 const float negm = kBiased ? -__builtin_fmaf(kI8Bias, c, m_eff) : -m_eff;
@@ -858,7 +897,7 @@ void fwd_kernel(const FwdParams p_in) {
             if (j < nkt_w) {
                 float ksj = 1.0f;
                 if constexpr (INT8) ksj = kscale[bhk * p.nkblk + (BMASK ? tile_row(j) / kBN : j)];
-                compute(j, kbuf((j + 1) & 1), vbuf(j & 1), ksj, std::false_type{});
+                compute(j, kbuf((j + 1) & 1), 0, vbuf(j & 1), ksj, std::false_type{});
             }
             sstore_k(j & 1, kreg[SS]);
             sstore_v((j + 1) & 1, vreg[SS]);
@@ -879,7 +918,7 @@ void fwd_kernel(const FwdParams p_in) {
             dtl_k(tile_row(j + NST), dks[J]);
             if constexpr (INT8) ksring[J] = kscale_at(j + NST);
             dtl_v(tile_row(j + NST - 1), dvs[(J + NST - 1) % NST]);
-            if (j < nkt_w) compute(j, dks[(J + 1) % NST], dvs[J], ksj, std::true_type{});
+            if (j < nkt_w) compute(j, dks[(J + 1) % NST], (J + 1) % NST % 2, dvs[J], ksj, std::true_type{});
         };
         if constexpr (DTL) {
             const int iters = geom::dtl_loop_iterations<NST>(nkt);
