@@ -201,25 +201,37 @@ __device__ __forceinline__ void dtl_copies(const char* base, const uint32_t (&of
 
 typedef const __attribute__((address_space(3))) char* lds_cptr;
 
-// FP16 scores of one 64-key tile as score_tile computes them (same MFMAs in
-// the same order), from per-lane LDS addresses of the K chunks the wave
-// reads at each k-step, given for query-row block 0 (block 1 lies 32 rows
-// further: the swizzle repeats every 32 rows at this row size).
-template <int D, int N, typename QF, typename ACC>
+// Scores of one 64-key tile (FP16 or INT8) as score_tile computes them (same
+// MFMAs in the same order), from per-lane LDS addresses of the K chunks the
+// wave reads at each k-step, given for query-row block 0 (block 1 lies 32
+// rows further: the swizzle repeats every 32 rows at these row sizes).
+template <int D, bool INT8, bool BIASED, int N, typename QF, typename ACC>
 __device__ __forceinline__ void score_tile_at(const lds_cptr (&ka)[N], const QF* qf, ACC* acc) {
-    using C = Cfg<D, false, false>;
+    using C = Cfg<D, INT8, false>;
     static_assert(N == C::QSTEPS, "one address per k-step");
     static_assert(32 % geom::Dtl<C::KROWG>::RPL == 0 && (32 / geom::Dtl<C::KROWG>::RPL) % geom::Dtl<C::KROWG>::CPR == 0,
                   "the K swizzle must repeat every 32 rows");
-    typedef const __attribute__((address_space(3))) h8 lds_h8;
-    acc[0] = typename C::acc_t{};
-    acc[1] = typename C::acc_t{};
+    static_assert(!BIASED || INT8, "the bias applies to INT32 accumulators");
+    if constexpr (BIASED) {
+        acc[0] = kI8BiasBits;
+        acc[1] = kI8BiasBits;
+    } else {
+        acc[0] = ACC{};
+        acc[1] = ACC{};
+    }
 #pragma unroll
     for (int s = 0; s < C::QSTEPS; ++s)
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-            const h8 a = *(lds_h8*)(ka[s] + mt * 32 * C::KROWG);
-            acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[s], acc[mt], 0, 0, 0);
+            if constexpr (INT8) {
+                typedef const __attribute__((address_space(3))) i4x lds_i4x;
+                const i4x a = *(lds_i4x*)(ka[s] + mt * 32 * C::KROWG);
+                acc[mt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[s], acc[mt], 0, 0, 0);
+            } else {
+                typedef const __attribute__((address_space(3))) h8 lds_h8;
+                const h8 a = *(lds_h8*)(ka[s] + mt * 32 * C::KROWG);
+                acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[s], acc[mt], 0, 0, 0);
+            }
         }
 }
 
@@ -542,14 +554,14 @@ void fwd_kernel(const FwdParams p_in) {
     };
     char* dks[3] = {dk0, dk1, dk2};
     char* dvs[3] = {dv0, dv1, dv2};
-    // FP16 head_dim 128 (two stages): the K read addresses of both stages,
+    // head_dim 128, FP16 or INT8 codes: the K read addresses of every stage,
     // computed once per item and kept in registers (opaque to the compiler,
     // which otherwise re-adds the stage base to each lane offset per tile).
-    constexpr bool KADDR = DTL && !INT8 && !F8 && D == 128 && NST == 2;
-    lds_cptr kaddr[2][C::QSTEPS];
+    constexpr bool KADDR = DTL && !F8 && D == 128;
+    lds_cptr kaddr[3][C::QSTEPS];
     if constexpr (KADDR) {
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+        for (int st = 0; st < NST; ++st)
 #pragma unroll
             for (int s = 0; s < C::QSTEPS; ++s) {
                 kaddr[st][s] = (lds_cptr)(dks[st] + l32 * C::KROWG + (((2 * s + g) ^ DK::k_swz(l32)) << 4));
@@ -792,7 +804,7 @@ void fwd_kernel(const FwdParams p_in) {
                 // row maxima (same-run A/B: +3-4 % on the 8192-token prefill).
                 __builtin_amdgcn_s_setprio(1);
                 acc_t sn[2];
-                if constexpr (KADDR && SWZ) score_tile_at<D>(kaddr[kst], qf, sn);
+                if constexpr (KADDR && SWZ) score_tile_at<D, INT8, kBiased>(kaddr[kst], qf, sn);
                 else score_tile<D, INT8, F8, kBiased, SWZ>(ksn, qf, l32, g, sn);
 
                 const float m_eff = BMASK && m_run == -INFINITY ? 0.0f : m_run;   // (masked rows: weights 0)
@@ -918,7 +930,7 @@ void fwd_kernel(const FwdParams p_in) {
             dtl_k(tile_row(j + NST), dks[J]);
             if constexpr (INT8) ksring[J] = kscale_at(j + NST);
             dtl_v(tile_row(j + NST - 1), dvs[(J + NST - 1) % NST]);
-            if (j < nkt_w) compute(j, dks[(J + 1) % NST], (J + 1) % NST % 2, dvs[J], ksj, std::true_type{});
+            if (j < nkt_w) compute(j, dks[(J + 1) % NST], (J + 1) % NST, dvs[J], ksj, std::true_type{});
         };
         if constexpr (DTL) {
             const int iters = geom::dtl_loop_iterations<NST>(nkt);
