@@ -594,16 +594,48 @@ int oracle_quant_attention_e4m3(int32_t B, int32_t Hq, int32_t Hkv, int32_t S, i
 /* a key is therefore rounded relative to the running maximum at its tile. */
 /* p_quant = 0 keeps p unrounded (then O equals exact attention on the     */
 /* same scores and V').  v_codes: [B,Hkv,S,D]; v_scale: [B,Hkv,D].         */
+/*                                                                          */
+/* tie_slack (nullable, one value per output row): a bound on how far the  */
+/* row's O may move when a weight whose 448 p lies within a relative        */
+/* distance tie_rel of a half-way point between two E4M3 values is rounded */
+/* to the other neighbour (as a computation of p with a relative error     */
+/* below tie_rel may do): the sum over those weights of one E4M3 step of   */
+/* the weight, carried to the final maximum like acc, times max_c |V'_jc|, */
+/* divided by l.  It is 0 for a row with no such weight.                   */
 /* ------------------------------------------------------------------------ */
+/* Spacing of the E4M3 grid around x (0 <= x <= 448): 2^(e-3) in the binade */
+/* [2^e, 2^(e+1)) of the normal numbers (e >= -6), 2^-9 among the          */
+/* subnormals below 2^-6.  Distance from x to the nearest half-way point   */
+/* between two neighbouring grid values of that binade.                    */
+static double e4m3_spacing(double x)
+{
+    if (x < 0.015625) return 0.001953125;
+    int e = 0;
+    frexp(x, &e);                 /* x = f 2^e, f in [0.5, 1): binade 2^(e-1) */
+    return ldexp(1.0, e - 1 - 3);
+}
+static double e4m3_tie_distance(double x)
+{
+    double sp = e4m3_spacing(x);
+    double base = 0.0;
+    if (x >= 0.015625) {
+        int e = 0;
+        frexp(x, &e);
+        base = ldexp(1.0, e - 1);
+    }
+    double u = (x - base) / sp;   /* position in grid steps within the binade */
+    return fabs((u - floor(u)) - 0.5) * sp;
+}
+
 int oracle_pv8_attention(int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t D,
                          const int8_t* q_i8, const float* q_scale, int32_t bq,
                          const int8_t* k_i8, const float* k_scale, int32_t bk,
                          const uint8_t* v_codes, const float* v_scale, const int32_t* kv_map,
                          int32_t causal, double sm_scale, int32_t tile, int32_t p_quant,
                          const int32_t* rows, int32_t nrows,
-                         double* out, double* lse, int32_t nthreads)
+                         double* out, double* lse, double tie_rel, double* tie_slack, int32_t nthreads)
 {
-    if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || D <= 0 || bq <= 0 || bk <= 0 || tile <= 0)
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || D <= 0 || bq <= 0 || bk <= 0 || tile <= 0 || tie_rel < 0.0)
         return -1;
     if (check_map(Hq, Hkv, kv_map)) return -4;
     if (!rows) nrows = S;
@@ -639,7 +671,7 @@ int oracle_pv8_attention(int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t 
                     for (int c = 0; c < D; ++c) dot += (int64_t)qp[c] * (int64_t)Kh[(int64_t)j * D + c];
                     s[j] = (double)dot * dq * (double)dk[j / bk] * sm_scale;
                 }
-                double m = -INFINITY, l = 0.0;
+                double m = -INFINITY, l = 0.0, slack = 0.0;
                 for (int c = 0; c < D; ++c) acc[c] = 0.0;
                 for (int32_t j0 = 0; j0 < nvis; j0 += tile) {
                     int32_t j1 = j0 + tile < nvis ? j0 + tile : nvis;
@@ -648,18 +680,27 @@ int oracle_pv8_attention(int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t 
                         if (s[j] > mt) mt = s[j];
                     double alpha = exp(m - mt);     /* exp(-inf) = 0 on the first tile */
                     l *= alpha;
+                    slack *= alpha;
                     for (int c = 0; c < D; ++c) acc[c] *= alpha;
                     for (int32_t j = j0; j < j1; ++j) {
                         double p = exp(s[j] - mt);
                         l += p;
                         double pq = p_quant ? oracle_e4m3_round(p * 448.0) / 448.0 : p;
-                        for (int c = 0; c < D; ++c)
-                            acc[c] += pq * (oracle_e4m3_decode(Vc[(int64_t)j * D + c]) * (double)dv[c]);
+                        double vmax = 0.0;
+                        for (int c = 0; c < D; ++c) {
+                            double vv = oracle_e4m3_decode(Vc[(int64_t)j * D + c]) * (double)dv[c];
+                            acc[c] += pq * vv;
+                            if (fabs(vv) > vmax) vmax = fabs(vv);
+                        }
+                        double x = p * 448.0;
+                        if (p_quant && e4m3_tie_distance(x) <= tie_rel * x)
+                            slack += e4m3_spacing(x) / 448.0 * vmax;
                     }
                     m = mt;
                 }
                 for (int c = 0; c < D; ++c) o[c] = acc[c] / l;
                 if (lse) lse[t] = m + log(l);
+                if (tie_slack) tie_slack[t] = slack / l;
             }
         }
         free(s); free(acc);

@@ -76,7 +76,7 @@ def lib():
         L.oracle_quant_attention_e4m3.argtypes = L.oracle_quant_attention.argtypes
         L.oracle_quant_attention_e4m3.restype = ctypes.c_int
         L.oracle_pv8_attention.argtypes = ([I32] * 5 + [P, P, I32, P, P, I32, P, P, P, I32, D, I32,
-                                           I32, P, I32, P, P, I32])
+                                           I32, P, I32, P, P, D, P, I32])
         L.oracle_pv8_attention.restype = ctypes.c_int
         L.oracle_attention_kv.argtypes = [I32] * 6 + [P, P, P, P, I32, D, P, P, I32]
         L.oracle_attention_kv.restype = ctypes.c_int
@@ -323,9 +323,14 @@ def quant_attention_fp8(qz, v, causal=False, kv_map=None, sm_scale=None, rows=No
 
 
 def pv8_attention(qz, v_codes, v_scale, causal=False, kv_map=None, sm_scale=None, rows=None,
-                  with_lse=False, bq=BQ, bk=BK, tile=BK, p_quant=True, nthreads=0):
+                  with_lse=False, bq=BQ, bk=BK, tile=BK, p_quant=True, tie_rel=None, nthreads=0):
     """O5: INT8 Q/K scores, 8-bit P (against the running maximum of the
-    online softmax over key tiles of `tile` keys) and 8-bit V."""
+    online softmax over key tiles of `tile` keys) and 8-bit V.
+
+    With tie_rel (a relative distance) it also returns, per output row, the
+    bound on how far O may move when weights whose 448 p lies within tie_rel
+    of an E4M3 half-way point round to the other neighbour: returns
+    (out, lse, slack) or (out, slack)."""
     qi = np.ascontiguousarray(qz["q_i8"])
     ki = np.ascontiguousarray(qz["k_i8"])
     qs = np.ascontiguousarray(qz["q_scale"], dtype=np.float32)
@@ -342,13 +347,17 @@ def pv8_attention(qz, v_codes, v_scale, causal=False, kv_map=None, sm_scale=None
     n = nr if r is not None else S
     out = np.empty((B, Hq, n, D), dtype=np.float64)
     lse = np.empty((B, Hq, n), dtype=np.float64) if with_lse else None
+    slack = np.empty((B, Hq, n), dtype=np.float64) if tie_rel is not None else None
     st = lib().oracle_pv8_attention(B, Hq, Hkv, S, D, _ptr(qi), _ptr(qs), bq, _ptr(ki), _ptr(ks), bk,
                                     _ptr(vc), _ptr(vs), _ptr(m), int(bool(causal)), float(sm_scale),
                                     int(tile), int(bool(p_quant)),
                                     _ptr(r) if r is not None else None, nr,
-                                    _ptr(out), _ptr(lse) if lse is not None else None, int(nthreads))
+                                    _ptr(out), _ptr(lse) if lse is not None else None,
+                                    float(tie_rel or 0.0), _ptr(slack) if slack is not None else None,
+                                    int(nthreads))
     _check(st, "pv8_attention")
-    return (out, lse) if with_lse else out
+    res = (out,) + ((lse,) if with_lse else ()) + ((slack,) if slack is not None else ())
+    return res if len(res) > 1 else out
 
 
 # --------------------------------------------------------------------------

@@ -8,11 +8,22 @@ and 8-bit P and V lose accuracy in some layers.  Here:
   the oracle, including half-way cases and the sign of zero.
 * attn_fwd_fp8: max-abs <= 2e-3 against the oracle's E4M3 quantised-attention
   model (same codes and scales), lse within 1e-4.
-* attn_fwd_int8_pv8: against the oracle's online 8-bit P.V model (O5):
-  relative L1 <= 2e-3 and cosine >= 0.99999.  Elementwise equality is not
-  expected: a weight whose fp32 value lies within a few ulps of an E4M3
-  half-way point may round to the other neighbour than in fp64 (about 1 in
-  2^18 weights), moving one output row by up to an E4M3 step of that weight.
+* attn_fwd_int8_pv8: element by element against the oracle's online 8-bit
+  P.V model (O5, each weight rounded to E4M3 against the running maximum of
+  its 64-key tile): |got - O5| <= 2e-3 + 2^-11 |O5| + slack(row).  The
+  middle term is the fp16 store of O (half an ulp, up to 2^-11 |O|): the
+  8-bit V' values are not fp16 numbers, and rows of a few keys reach |O| > 4,
+  where that rounding alone approaches 2e-3.  The kernel forms each
+  weight in fp32 with a relative error below 2^-13 for inputs of these
+  magnitudes (|Q| and the smoothed |K| below about 5): it is dominated by the
+  rounding of the fp32 sum of the INT32-score bias times the dequantisation
+  factor and the running maximum, half an ulp of a value below 4096, i.e. at
+  most 2^-13 in log2 units.  A weight can therefore round to the other E4M3
+  neighbour than in fp64 only when 448 p lies within that distance of a
+  half-way point; O5 reports, per row, one E4M3 step of every weight within
+  2^-11 (four times that) of a half-way point, carried to the final maximum
+  and times the row's largest |V'|, over l.  Rows without such a weight
+  (slack 0) are held to 2e-3 alone.
 * The pages' claims on the GPU results: INT8 Q/K is closer to exact attention
   than FP8 Q/K and than 8-bit P.V.
 """
@@ -29,8 +40,8 @@ from _util import case, cos_rel_l1, dev, host, small_workload
 pytestmark = pytest.mark.gpu
 
 FP8_VS_MODEL_MAX_ABS = 2e-3
-PV8_VS_MODEL_REL_L1 = 2e-3
-PV8_VS_MODEL_COS = 0.99999
+PV8_VS_MODEL_MAX_ABS = 2e-3
+PV8_TIE_REL = 2.0 ** -11
 
 SHAPES = [(1, 2, 2, 1, 64, False), (1, 2, 1, 17, 128, True), (1, 4, 2, 63, 64, True),
           (1, 2, 2, 64, 128, False), (2, 4, 1, 65, 64, True), (1, 2, 2, 129, 128, True),
@@ -149,10 +160,18 @@ def _pv8_check(w, q, k, v, rows=None, kv_map=None):
         got, gl = got[:, :, rows], gl[:, :, rows]
     qz_h = {key: host(qz[key]) for key in ("q_i8", "q_scale", "k_i8", "k_scale")}
     codes, sc = O.quant_v_fp8(v)
-    model, ml = O.pv8_attention(qz_h, codes, sc, causal=w.causal, kv_map=kv_map, rows=rows,
-                                with_lse=True)
-    cos, rel = cos_rel_l1(got, model)
-    assert cos >= PV8_VS_MODEL_COS and rel <= PV8_VS_MODEL_REL_L1, (cos, rel)
+    model, ml, slack = O.pv8_attention(qz_h, codes, sc, causal=w.causal, kv_map=kv_map, rows=rows,
+                                       with_lse=True, tie_rel=PV8_TIE_REL)
+    err = np.abs(got - model)
+    bound = PV8_VS_MODEL_MAX_ABS + 2.0 ** -11 * np.abs(model) + slack[..., None]
+    flagged = slack > 0
+    row_err = err.max(axis=-1)
+    print(f"[pv8] {w.name}: {int(flagged.sum())} of {flagged.size} rows hold a near-tie weight; "
+          f"max err {row_err.max():.2e} (rows without: {row_err[~flagged].max() if (~flagged).any() else 0:.2e})",
+          flush=True)
+    bad = err > bound
+    assert not bad.any(), (f"{int(bad.sum())} elements outside 2e-3 + 2^-11 |O5| + slack; worst excess "
+                           f"{(err - bound).max()} at {np.argwhere(bad)[0]}")
     assert np.abs(gl - ml).max() <= 1e-4
     return got
 

@@ -9,6 +9,9 @@ P as E4M3(448 p) / 448 against the online softmax's running maximum, 8-bit V
 with one scale per channel) are pinned here against torch's independent
 float8_e4m3fn conversion, exact grids, closed forms and error bounds.
 """
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
 import numpy as np
 import pytest
 import torch
@@ -291,6 +294,133 @@ def test_pv8_weight_rounding_error_bound(causal):
     bound = (2.0 ** -4 + n * 2.0 ** -10 / 448) * vmax
     assert np.all(np.abs(o_r - o_u).max(axis=-1) <= bound[None, None, :] * (1 + 1e-9))
     assert np.abs(o_r - o_u).max() > 0          # the rounding does act
+
+
+# --------------------------------------------------------------------------
+# O5's rounding point, pinned by a hand computation
+# --------------------------------------------------------------------------
+def _e4m3_grid():
+    """Every non-negative finite E4M3 value from the format's definition
+    (exponent bias 7, 3 mantissa bits, subnormals m/8 * 2^-6, exponent field
+    15 with mantissa 7 the NaN, so 448 is the largest value), exactly."""
+    vals = [Fraction(m, 8) * Fraction(1, 64) for m in range(8)]
+    for e in range(1, 16):
+        for m in range(8):
+            if not (e == 15 and m == 7):
+                vals.append((1 + Fraction(m, 8)) * Fraction(2) ** (e - 7))
+    return sorted(vals)
+
+
+_GRID = _e4m3_grid()
+
+
+def _round_and_tie(x: Decimal):
+    """Nearest E4M3 value of 0 < x <= 448 (exact; no tie may occur here), the
+    larger of the grid gaps on either side of it (the most a rounding to the
+    other side can move it) and x's relative distance from the nearest
+    half-way point between two neighbouring grid values."""
+    xf = Fraction(x)
+    hi = next(i for i, g in enumerate(_GRID) if g >= xf)
+    if xf == _GRID[hi]:                      # on the grid: the half-way points on either side
+        gaps = [_GRID[hi] - _GRID[hi - 1]] + ([_GRID[hi + 1] - _GRID[hi]] if hi + 1 < len(_GRID) else [])
+        return xf, max(gaps), min(gaps) / 2 / xf
+    below, above = _GRID[hi - 1], _GRID[hi]
+    assert abs((xf - below) - (above - xf)) > Fraction(1, 10 ** 30) * xf, "a tie"
+    nearest = below if xf - below < above - xf else above
+    return nearest, above - below, abs(xf - (below + above) / 2) / xf
+
+
+def _hand_pv8(a, vq, tile, tie_rel=None):
+    """O of one query row in closed form, 50-digit decimals: scores a_j ln2/8
+    (so exp(s_j - m) = 2^((a_j - m)/8)); key j is weighted by
+    E4M3(448 2^((a_j - M_t)/8)) / 448 * 2^((M_t - M)/8), where M_t is the
+    maximum of the scores up to the end of j's tile of `tile` keys and M the
+    row maximum; l = sum_j 2^((a_j - M)/8) (unrounded).  Also the tie slack of
+    the weights whose 448 p lies within tie_rel of a half-way point."""
+    getcontext().prec = 50
+    two = Decimal(2)
+    n = len(a)
+    M = max(a)
+    l = sum(two ** (Decimal(int(x - M)) / 8) for x in a)
+    acc = [Decimal(0)] * vq.shape[1]
+    slack = Decimal(0)
+    rel = []
+    for j in range(n):
+        Mt = max(a[:min(n, (j // tile + 1) * tile)])
+        x = 448 * two ** (Decimal(int(a[j] - Mt)) / 8)
+        r, step, d = _round_and_tie(x)
+        carry = two ** (Decimal(int(Mt - M)) / 8)
+        w = Decimal(r.numerator) / Decimal(r.denominator) / 448 * carry
+        for c in range(vq.shape[1]):
+            acc[c] += w * Decimal(float(vq[j, c]))
+        rel.append(d)
+        if tie_rel is not None and d <= Fraction(tie_rel):
+            slack += Decimal(step.numerator) / Decimal(step.denominator) / 448 * carry * \
+                Decimal(float(np.abs(vq[j]).max()))
+    return np.array([float(x / l) for x in acc]), float(slack / l), rel
+
+
+def _two_tile_case():
+    """One row over 128 keys (two 64-key tiles): keys 0-31 peak at 40, keys
+    32-63 at 60 and keys 64-127 at 75, so the running maximum rises inside the
+    first 64 keys (at a 32-key boundary) and again in the second tile, by
+    amounts that are not multiples of 8 (the rescale factors are not powers of
+    two, which rounding would commute with)."""
+    rng = np.random.default_rng(2025)
+    S, D = 128, 16
+    a = np.concatenate([rng.integers(0, 41, 32), rng.integers(10, 61, 32), rng.integers(30, 76, 64)])
+    a[5], a[40], a[100] = 40, 60, 75
+    q_i8 = np.zeros((1, 1, S, D), np.int8)
+    q_i8[..., 0] = 1
+    k_i8 = np.zeros((1, 1, S, D), np.int8)
+    k_i8[0, 0, :, 0] = a
+    qz = dict(q_i8=q_i8, q_scale=np.ones((1, 1, 1), np.float32), k_i8=k_i8,
+              k_scale=np.ones((1, 1, 2), np.float32))
+    finite = _finite_codes()
+    mag = finite[(O.e4m3_decode(finite) >= 0.25) & (O.e4m3_decode(finite) <= 4)]
+    codes = rng.choice(mag, (1, 1, S, D)).astype(np.uint8)
+    vq = _torch_decode(codes)[0, 0]
+    return qz, codes, np.ones((1, 1, D), np.float32), a, vq
+
+
+def test_pv8_rounds_each_weight_against_the_running_maximum_of_its_64_key_tile():
+    """R20 pinned: O5 equals the closed form with 64-key tiles (the running
+    maximum at the end of each key's tile), and that value differs from both
+    alternative readings -- 32-key tiles, and rounding against the final row
+    maximum -- by far more than the comparison's tolerance, so O5 computed
+    under either of them fails this test.  O5 with tile = 32 and tile = 128
+    (one tile: the final maximum) matches the closed form of that reading
+    too, which checks the closed form itself."""
+    qz, codes, vs, a, vq = _two_tile_case()
+    sm = float(np.log(2.0) / 8)
+    hand = {t: _hand_pv8(list(a), vq, t)[0] for t in (64, 32, 128)}
+    for t in (64, 32, 128):
+        o5 = O.pv8_attention(qz, codes, vs, sm_scale=sm, tile=t, rows=np.array([0], np.int32))[0, 0, 0]
+        np.testing.assert_allclose(o5, hand[t], rtol=0, atol=1e-12)
+    assert np.abs(hand[64] - hand[32]).max() > 1e-4
+    assert np.abs(hand[64] - hand[128]).max() > 1e-4
+    o5 = O.pv8_attention(qz, codes, vs, sm_scale=sm, rows=np.array([0], np.int32))[0, 0, 0]   # default tile
+    np.testing.assert_allclose(o5, hand[64], rtol=0, atol=1e-12)
+
+
+def test_pv8_tie_slack_against_the_hand_computation():
+    """The per-row tie slack: 0 at tie_rel = 0; with tie_rel just above the
+    k-th smallest relative distance of a weight from an E4M3 half-way point
+    it sums exactly the k weights that close (one grid step each, carried to
+    the final maximum, times the row's largest |V'|, over l)."""
+    qz, codes, vs, a, vq = _two_tile_case()
+    sm = float(np.log(2.0) / 8)
+    row = np.array([0], np.int32)
+    _, s0 = O.pv8_attention(qz, codes, vs, sm_scale=sm, rows=row, tie_rel=0.0)
+    assert s0[0, 0, 0] == 0.0
+    _, _, rel = _hand_pv8(list(a), vq, 64)
+    order = sorted(float(r) for r in rel)
+    for k in (1, 5, 20, 128):
+        tie_rel = order[k - 1] * (1 + 1e-9) if k < 128 else 1.0
+        _, hand_slack, _ = _hand_pv8(list(a), vq, 64, tie_rel=tie_rel)
+        _, sl = O.pv8_attention(qz, codes, vs, sm_scale=sm, rows=row, tie_rel=tie_rel)
+        np.testing.assert_allclose(sl[0, 0, 0], hand_slack, rtol=1e-12, atol=0)
+    assert hand_slack > 0
 
 
 # --------------------------------------------------------------------------
