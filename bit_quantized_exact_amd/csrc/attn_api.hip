@@ -147,6 +147,32 @@ void set_workspace(DecParams* p, void* workspace, int D) {
     p->ws_l = reinterpret_cast<float*>(w + dec::ws_l_offset(rows, D));
 }
 
+// The INT32 score dump of the INT8 forward (from INT8 Q, or fp16 Q quantised
+// in the kernel) for query tiles q_tile_lo..q_tile_hi.
+int debug_dump(const attn_shape* shape, const void* q, bool fused_q, const int8_t* k_i8,
+               const int32_t* kv_head_map, int causal, int32_t q_tile_lo, int32_t q_tile_hi,
+               int32_t* s_out, float* q_scale_out, void* stream) {
+    int st = check_shape(shape);
+    if (st != ATTN_OK) return st;
+    if (!q || !k_i8 || !s_out) return ATTN_EINVAL;
+    if (!aligned(q, 16) || !aligned(k_i8, 16) || !aligned(s_out, 4) || (q_scale_out && !aligned(q_scale_out, 4)))
+        return ATTN_EINVAL;
+    const int nqt = ceil_div(shape->seq, kBM);
+    if (q_tile_lo < 0 || q_tile_hi < q_tile_lo || q_tile_hi >= nqt) return ATTN_EINVAL;
+    FwdParams p;
+    std::memset(&p, 0, sizeof(p));
+    if ((st = build_map(*shape, kv_head_map, &p)) != ATTN_OK) return st;
+    fill_common(*shape, &p);
+    p.q = q;
+    p.k = k_i8;
+    p.s_out = s_out;
+    p.q_scale_out = q_scale_out;
+    p.tile_lo = q_tile_lo;
+    p.ntiles = q_tile_hi - q_tile_lo + 1;
+    return launch_fwd(fused_q ? FwdKind::kDumpInt8FusedQ : FwdKind::kDumpInt8, shape->head_dim, causal != 0, p,
+                      static_cast<hipStream_t>(stream));
+}
+
 }  // namespace
 }  // namespace attn
 
@@ -276,22 +302,16 @@ int attn_fwd_fp16(const attn_shape* shape, const void* q_f16, const void* k_f16,
 int attn_debug_qk_int32(const attn_shape* shape, const int8_t* q_i8, const int8_t* k_i8,
                         const int32_t* kv_head_map, int causal, int32_t q_tile_lo,
                         int32_t q_tile_hi, int32_t* s_out, void* stream) {
-    int st = check_shape(shape);
-    if (st != ATTN_OK) return st;
-    if (!q_i8 || !k_i8 || !s_out) return ATTN_EINVAL;
-    if (!aligned(q_i8, 16) || !aligned(k_i8, 16) || !aligned(s_out, 4)) return ATTN_EINVAL;
-    const int nqt = ceil_div(shape->seq, kBM);
-    if (q_tile_lo < 0 || q_tile_hi < q_tile_lo || q_tile_hi >= nqt) return ATTN_EINVAL;
-    FwdParams p;
-    std::memset(&p, 0, sizeof(p));
-    if ((st = build_map(*shape, kv_head_map, &p)) != ATTN_OK) return st;
-    fill_common(*shape, &p);
-    p.q = q_i8;
-    p.k = k_i8;
-    p.s_out = s_out;
-    p.tile_lo = q_tile_lo;
-    p.ntiles = q_tile_hi - q_tile_lo + 1;
-    return launch_fwd(FwdKind::kDumpInt8, shape->head_dim, causal != 0, p, static_cast<hipStream_t>(stream));
+    return debug_dump(shape, q_i8, false, k_i8, kv_head_map, causal, q_tile_lo, q_tile_hi, s_out, nullptr,
+                      stream);
+}
+
+int attn_debug_qk_int32_fused_q(const attn_shape* shape, const void* q_f16, const int8_t* k_i8,
+                                const int32_t* kv_head_map, int causal, int32_t q_tile_lo,
+                                int32_t q_tile_hi, int32_t* s_out, float* q_scale_out,
+                                void* stream) {
+    return debug_dump(shape, q_f16, true, k_i8, kv_head_map, causal, q_tile_lo, q_tile_hi, s_out, q_scale_out,
+                      stream);
 }
 
 int attn_quantize_qk_fp8(const attn_shape* shape, const void* q_f16, const void* k_f16,

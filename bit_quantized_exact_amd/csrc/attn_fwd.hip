@@ -163,35 +163,43 @@ __device__ __forceinline__ void lds_stage_barrier() {
 // compiler's wait counting treats every LDS read as unordered while such a
 // copy is in flight and drains all LDS reads (lgkmcnt(0)) wherever it waits
 // for one; the copies' completion is tracked by the explicit waits of
-// lds_stage_barrier in any case.  The s_nop 4 at the head of the block
-// covers the wait states after a vector instruction that wrote an SGPR the
-// copies read (every input is written before the block; the hazard
-// recognizer does not look at asm inputs), each s_nop 0 the M0 write before
-// an LDS DMA.
+// lds_stage_barrier in any case.  The copies take their LDS address from
+// M0, which the compiler reserves (it ignores M0 in a clobber list), so each
+// block saves M0 into an SGPR of its own at its head and restores it at its
+// tail: no value the compiler keeps in M0 is changed.  The s_nop 4 covers
+// the wait states after a vector instruction that wrote an SGPR the copies
+// read (every input is written before the block; the hazard recognizer does
+// not look at asm inputs), each s_nop 0 the M0 write before an LDS DMA.
 template <int N>
 __device__ __forceinline__ void dtl_copies(const char* base, const uint32_t (&off)[N], const char* lds) {
     static_assert(N == 1 || N == 2 || N == 4, "copies per block");
     const uint32_t l0 = static_cast<uint32_t>(
         reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)lds));
+    uint32_t saved_m0;
     if constexpr (N == 1) {
-        asm volatile("s_nop 4\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-                     :: "v"(off[0]), "s"(base), "s"(l0) : "memory", "m0");
+        asm volatile("s_mov_b32 %0, m0\n\ts_nop 4\n\t"
+                     "s_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\t"
+                     "s_mov_b32 m0, %0"
+                     : "=&s"(saved_m0) : "v"(off[0]), "s"(base), "s"(l0) : "memory");
     } else if constexpr (N == 2) {
         const uint32_t l1 = l0 + 1024;
-        asm volatile("s_nop 4\n\t"
-                     "s_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2\n\t"
-                     "s_mov_b32 m0, %4\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                     :: "v"(off[0]), "v"(off[1]), "s"(base), "s"(l0), "s"(l1) : "memory", "m0");
+        asm volatile("s_mov_b32 %0, m0\n\ts_nop 4\n\t"
+                     "s_mov_b32 m0, %4\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %3\n\t"
+                     "s_mov_b32 m0, %5\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\t"
+                     "s_mov_b32 m0, %0"
+                     : "=&s"(saved_m0) : "v"(off[0]), "v"(off[1]), "s"(base), "s"(l0), "s"(l1) : "memory");
     } else {
         const uint32_t l1 = l0 + 1024, l2 = l0 + 2048, l3 = l0 + 3072;
-        asm volatile("s_nop 4\n\t"
-                     "s_mov_b32 m0, %5\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %4\n\t"
-                     "s_mov_b32 m0, %6\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %4\n\t"
-                     "s_mov_b32 m0, %7\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %4\n\t"
-                     "s_mov_b32 m0, %8\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %3, %4"
-                     :: "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "s"(base), "s"(l0), "s"(l1),
-                        "s"(l2), "s"(l3)
-                     : "memory", "m0");
+        asm volatile("s_mov_b32 %0, m0\n\ts_nop 4\n\t"
+                     "s_mov_b32 m0, %6\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %5\n\t"
+                     "s_mov_b32 m0, %7\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %5\n\t"
+                     "s_mov_b32 m0, %8\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %3, %5\n\t"
+                     "s_mov_b32 m0, %9\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %4, %5\n\t"
+                     "s_mov_b32 m0, %0"
+                     : "=&s"(saved_m0)
+                     : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "s"(base), "s"(l0), "s"(l1),
+                       "s"(l2), "s"(l3)
+                     : "memory");
     }
 }
 
@@ -304,7 +312,7 @@ template <int D, bool INT8, bool CAUSAL, bool DUMP, bool QF16 = false, bool F8 =
 __global__ __launch_bounds__(kFwdThreads)
 __attribute__((amdgpu_waves_per_eu(fwd_waves(D, INT8, CAUSAL, BMASK), fwd_waves(D, INT8, CAUSAL, BMASK))))
 void fwd_kernel(const FwdParams p_in) {
-    static_assert(!QF16 || (INT8 && !DUMP), "in-kernel Q quantisation is an INT8 forward variant");
+    static_assert(!QF16 || INT8, "in-kernel Q quantisation is an INT8 forward variant");
     static_assert(!F8 || (INT8 && !DUMP && !QF16 && !PV8), "FP8 scores: standalone-quantised Q/K");
     static_assert(!PV8 || (INT8 && !DUMP && !QF16 && !F8), "8-bit P.V: INT8 Q/K");
     static_assert(!BMASK || (!CAUSAL && !DUMP && !QF16 && !F8 && !PV8), "tile masks: FP16 or two-call INT8");
@@ -314,20 +322,25 @@ void fwd_kernel(const FwdParams p_in) {
     typedef typename C::acc_t acc_t;
     // Staging: direct-to-LDS copies into unpadded swizzled stages (NST of
     // them, one array each so that the compiler can tell the copies of
-    // different stages apart), or the register path into padded tiles (the
-    // score dump, and tile-mask lists too long for their LDS copy).
+    // different stages apart), or the register path into padded tiles
+    // (tile-mask lists too long for their LDS copy).  The INT32 score dump
+    // (DUMP) runs the direct-to-LDS INT8 pipeline of the forward itself --
+    // the same K copies, stages, swizzle and score MFMAs, with or without
+    // the in-kernel Q quantisation -- and writes each tile's INT32 scores
+    // instead of running the softmax and P.V (it copies no V tiles).
     // (the tile-masked variant stages directly only with its key-tile list
     // copied into LDS first (MLDS): read per iteration from global memory, the
     // wave-uniform entry loads would become vector loads queued behind the
     // copies into LDS; lists too long for the LDS copy keep the register path)
-    constexpr bool DTL = ATTN_FWD_DTL && !DUMP && (!BMASK || MLDS);
+    constexpr bool DTL = ATTN_FWD_DTL && (!BMASK || MLDS);
+    static_assert(!DUMP || (DTL && INT8 && !F8 && !PV8), "the score dump runs the direct-to-LDS INT8 forward");
     static_assert(!PV8 || DTL, "the 8-bit P.V variant stages its V^T tiles directly into LDS");
     __shared__ int mlist[MLDS ? geom::kMaskListMax : 1];
 #ifndef ATTN_FWD_NST_F16_D128
 #define ATTN_FWD_NST_F16_D128 2
 #endif
     constexpr int NST = (!INT8 && D == 128) ? ATTN_FWD_NST_F16_D128 : 3;
-    __shared__ __attribute__((aligned(16))) char smem[DTL ? 16 : 2 * C::KBYTES + (DUMP ? 0 : 2 * C::VBYTES)];
+    __shared__ __attribute__((aligned(16))) char smem[DTL ? 16 : 2 * C::KBYTES + 2 * C::VBYTES];
     __shared__ __attribute__((aligned(16))) char dk0[DTL ? C::KSTAGE : 16], dk1[DTL ? C::KSTAGE : 16],
         dk2[DTL && NST == 3 ? C::KSTAGE : 16];
     __shared__ __attribute__((aligned(16))) char dv0[DTL ? C::VSTAGE : 16], dv1[DTL ? C::VSTAGE : 16],
@@ -340,7 +353,7 @@ void fwd_kernel(const FwdParams p_in) {
     // per workgroup in the snake order of geom::make_sched: the dispatch gap
     // between workgroups then recurs per several items, and the heaviest-
     // first query tiles pair up with light ones.
-    constexpr bool PERSIST = CAUSAL && !DUMP && !BMASK;
+    constexpr bool PERSIST = CAUSAL && !BMASK;
     const geom::Sched sched = geom::make_sched(blockIdx.x, gridDim.x, p_in.B * p_in.Hq * p_in.ntiles);
     const int n_iter = PERSIST ? geom::sched_iters(sched) : 1;
     for (int it = 0; it < n_iter; ++it) {
@@ -370,7 +383,7 @@ void fwd_kernel(const FwdParams p_in) {
     float scale_log2 = p.scale_log2;
     if constexpr (PERSIST) asm volatile("" : "+s"(scale_log2));
     // (tile masks are mostly causal-like too, heavier for later query tiles)
-    const geom::BlockCoord bc = geom::decode_item(item, p.Hq, p.ntiles, p.tile_lo, (CAUSAL || BMASK) && !DUMP);
+    const geom::BlockCoord bc = geom::decode_item(item, p.Hq, p.ntiles, p.tile_lo, CAUSAL || BMASK);
     const int b = bc.b;
     const int h = p.horder[bc.pos];
     const int kvh = p.kvmap[h];
@@ -436,7 +449,7 @@ void fwd_kernel(const FwdParams p_in) {
     // Addresses: a wave-uniform tile base plus a 32-bit per-lane offset
     // (row clamped to the sequence), so the loads use the scalar-base form.
     // Register sets for staging (a second set when prefetching two tiles ahead).
-    constexpr int DEPTH = DUMP ? 1 : geom::fwd_prefetch_depth(D, INT8);
+    constexpr int DEPTH = geom::fwd_prefetch_depth(D, INT8);
     i4x kreg[DEPTH][C::KPT], vreg[DEPTH][C::VPT];
     auto gload_k = [&](int n0, i4x (&dst)[C::KPT]) {
         const int first = geom::tile_first_row(n0, S);
@@ -522,8 +535,9 @@ void fwd_kernel(const FwdParams p_in) {
         dtl_copies<DK::NI>(base, off, st + wave_s * DK::NI * 1024);
     };
     using D8 = geom::Dtl8<D>;
-    constexpr int VNI = PV8 ? D8::NI : DV::NI;   // V copy instructions per wave per tile
+    constexpr int VNI = DUMP ? 0 : PV8 ? D8::NI : DV::NI;   // V copy instructions per wave per tile
     auto dtl_v = [&](int n0, char* st) __attribute__((always_inline)) {
+        if constexpr (DUMP) return;   // (the score dump needs no V)
         if constexpr (PV8) {
             // D rows of 64 key codes of the V^T tile at column v8_tile_col
             const char* base = vg + geom::v8_tile_col(n0, p.nkblk);
@@ -592,11 +606,11 @@ void fwd_kernel(const FwdParams p_in) {
     };
     if constexpr (DTL && !QFIRST) {
         dtl_prologue();
-        if constexpr (INT8) {
+        if constexpr (INT8 && !DUMP) {
 #pragma unroll
             for (int t = 0; t < NST; ++t) ksring[t] = kscale_at(t);
         }
-    } else if constexpr (!DTL && !DUMP) {
+    } else if constexpr (!DTL) {
         gload_k(tile_row(0), kreg[0]);
     }
 
@@ -680,37 +694,14 @@ void fwd_kernel(const FwdParams p_in) {
     auto mask_limit = [&](int n0) { return geom::mask_limit(n0, S, qi, g, CAUSAL); };
     auto tile_needs_mask = [&](int n0) { return (n0 + kBN > S) || (CAUSAL && n0 + kBN - 1 > qw0); };
 
-    if constexpr (DUMP) {
-        // ---- INT32 score dump: the same tile code, results written out ----
-        for (int j = 0; j < nkt; ++j) {
-            const int n0 = j * kBN;
-            gload_k(n0, kreg[0]);
-            sstore_k(0, kreg[0]);
-            __syncthreads();
-            if (j < nkt_w) {   // wave-uniform: the MFMAs run with every lane active
-                acc_t acc[2];
-                score_tile<D, INT8>(kbuf(0), qf, l32, g, acc);
-                if (qi < S) {
-                    int32_t* orow = p.s_out + (bhq * p.ntiles * kBM + (qi - p.tile_lo * kBM)) * static_cast<size_t>(S);
-                    const int lim = mask_limit(n0);
-#pragma unroll
-                    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            if (key_offset(mt, r) < lim) orow[n0 + g * 4 + key_offset(mt, r)] = acc[mt][r];
-                }
-            }
-            __syncthreads();
-        }
-        continue;
-    } else {
+    {
         float m_run = -INFINITY;   // running row max (log2 units); equal in lanes l and l^32
         float l_run = 0.0f;        // this lane's partial row sum
         f16x oacc[C::DT];
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) oacc[dt] = f16x{};
         float qscale = 1.0f;
-        if constexpr (INT8) qscale = QF16 ? qscale_fused : p.q_scale[bhq * p.nqblk + qt];
+        if constexpr (INT8 && !DUMP) qscale = QF16 ? qscale_fused : p.q_scale[bhq * p.nqblk + qt];
         const float* kscale = p.k_scale;
 
         // ---- prologue: K_0 -> LDS, S_0, then K_1 and V_0 -> LDS (and, at
@@ -749,7 +740,27 @@ void fwd_kernel(const FwdParams p_in) {
                            __attribute__((always_inline)) {
             constexpr bool SWZ = decltype(swz_tag)::value;
             const int n0 = tile_row(j);
-            {
+            if constexpr (DUMP) {
+                // the INT32 scores of tile j (accumulator bits minus the bias
+                // bits: the accumulation started at 0x4B400000 and |S32| < 2^22)
+                // for the visible keys of this lane's query row, then the next
+                // tile's scores exactly as the forward computes them
+                if (qi < S) {
+                    int32_t* orow = p.s_out + (bhq * p.ntiles * kBM + (qi - p.tile_lo * kBM)) * static_cast<size_t>(S);
+                    const int lim = mask_limit(n0);
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            if (key_offset(mt, r) < lim)
+                                orow[n0 + g * 4 + key_offset(mt, r)] = static_cast<int>(sc[mt][r]) - kI8BiasBits;
+                }
+                acc_t sn[2];
+                if constexpr (KADDR && SWZ) score_tile_at<D, INT8, kBiased>(kaddr[kst], qf, sn);
+                else score_tile<D, INT8, F8, kBiased, SWZ>(ksn, qf, l32, g, sn);
+                sc[0] = sn[0];
+                sc[1] = sn[1];
+            } else {
                 // scores in log2 units: s * c with c = (dQ dK) sm_scale log2(e)
                 float c = scale_log2;
                 if constexpr (INT8) c = fmaxf(qscale * kscale_j * scale_log2, FLT_MIN);
@@ -926,9 +937,11 @@ void fwd_kernel(const FwdParams p_in) {
         auto dstep = [&](int j, auto j_tag) __attribute__((always_inline)) {
             constexpr int J = decltype(j_tag)::value;
             const float ksj = ksring[J];
-            lds_stage_barrier<NST == 3 ? DK::NI + VNI + (INT8 ? 1 : 0) : 0>();
+            // (the score dump drains every copy: its global stores share the
+            // vector-memory counter with the copies)
+            lds_stage_barrier<(NST == 3 && !DUMP) ? DK::NI + VNI + (INT8 ? 1 : 0) : 0>();
             dtl_k(tile_row(j + NST), dks[J]);
-            if constexpr (INT8) ksring[J] = kscale_at(j + NST);
+            if constexpr (INT8 && !DUMP) ksring[J] = kscale_at(j + NST);
             dtl_v(tile_row(j + NST - 1), dvs[(J + NST - 1) % NST]);
             if (j < nkt_w) compute(j, dks[(J + 1) % NST], (J + 1) % NST, dvs[J], ksj, std::true_type{});
         };
@@ -953,32 +966,34 @@ void fwd_kernel(const FwdParams p_in) {
         // compiler from using scalar loads for the per-tile K scales)
         if constexpr (QF16)
             if (p.q_scale_out && tid == 0) p.q_scale_out[bhq * p.nqblk + qt] = qscale_fused;
-        const float l_tot = row_sum(l_run);
-        // (a row of a tile-masked query tile may see no key: O = 0, lse = -inf)
-        const float inv = BMASK && !(l_tot > 0.0f) ? 0.0f : 1.0f / l_tot;
-        if (qi < S) {
-            _Float16* orow = static_cast<_Float16*>(p.o) + (bhq * S + static_cast<size_t>(qi)) * D;
-            if constexpr (PV8) {
-                // undo the 448 of P8 and apply the per-channel V scales
-                const float* vsc = p.v_scale + bhk * D;
+        if constexpr (!DUMP) {
+            const float l_tot = row_sum(l_run);
+            // (a row of a tile-masked query tile may see no key: O = 0, lse = -inf)
+            const float inv = BMASK && !(l_tot > 0.0f) ? 0.0f : 1.0f / l_tot;
+            if (qi < S) {
+                _Float16* orow = static_cast<_Float16*>(p.o) + (bhq * S + static_cast<size_t>(qi)) * D;
+                if constexpr (PV8) {
+                    // undo the 448 of P8 and apply the per-channel V scales
+                    const float* vsc = p.v_scale + bhk * D;
+#pragma unroll
+                    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+                        for (int j4 = 0; j4 < 4; ++j4) {
+                            const int col = geom::o_column(dt, j4, g);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) oacc[dt][j4 * 4 + e] *= vsc[col + e] * (1.0f / 448.0f);
+                        }
+                }
 #pragma unroll
                 for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
                     for (int j4 = 0; j4 < 4; ++j4) {
-                        const int col = geom::o_column(dt, j4, g);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) oacc[dt][j4 * 4 + e] *= vsc[col + e] * (1.0f / 448.0f);
+                        const h2 a = __builtin_convertvector((f2){oacc[dt][j4 * 4 + 0] * inv, oacc[dt][j4 * 4 + 1] * inv}, h2);
+                        const h2 bb = __builtin_convertvector((f2){oacc[dt][j4 * 4 + 2] * inv, oacc[dt][j4 * 4 + 3] * inv}, h2);
+                        *reinterpret_cast<h4*>(orow + geom::o_column(dt, j4, g)) = __builtin_shufflevector(a, bb, 0, 1, 2, 3);
                     }
+                if (p.lse && g == 0) p.lse[bhq * S + qi] = (m_run + __builtin_log2f(l_tot)) * kLn2;
             }
-#pragma unroll
-            for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-                for (int j4 = 0; j4 < 4; ++j4) {
-                    const h2 a = __builtin_convertvector((f2){oacc[dt][j4 * 4 + 0] * inv, oacc[dt][j4 * 4 + 1] * inv}, h2);
-                    const h2 bb = __builtin_convertvector((f2){oacc[dt][j4 * 4 + 2] * inv, oacc[dt][j4 * 4 + 3] * inv}, h2);
-                    *reinterpret_cast<h4*>(orow + geom::o_column(dt, j4, g)) = __builtin_shufflevector(a, bb, 0, 1, 2, 3);
-                }
-            if (p.lse && g == 0) p.lse[bhq * S + qi] = (m_run + __builtin_log2f(l_tot)) * kLn2;
         }
         // no copy into LDS may still be landing when the workgroup ends (the
         // last iterations' copies of tiles past the end drain under the stores)
@@ -1008,7 +1023,7 @@ void launch_one(const FwdParams& p, hipStream_t st) {
     // workgroup (measured on the prefill shapes from 512 to 32768 tokens:
     // +5 to +20 %; three or more per workgroup, or non-causal launches, gain
     // nothing or lose to the slower tail)
-    const bool two = CAUSAL && !DUMP && !BMASK && items >= 8 * device_compute_units();
+    const bool two = CAUSAL && !BMASK && items >= 8 * device_compute_units();
     const int grid = two ? geom::sched_grid(items, (items + 1) / 2) : items;
     hipLaunchKernelGGL((fwd_kernel<D, INT8, CAUSAL, DUMP, QF16, F8, PV8, BMASK, MLDS>), dim3(grid),
                        dim3(kFwdThreads), 0, st, p);
@@ -1025,6 +1040,9 @@ void launch_d(FwdKind kind, bool causal, const FwdParams& p, hipStream_t st) {
             break;
         case FwdKind::kDumpInt8:
             causal ? launch_one<D, true, true, true>(p, st) : launch_one<D, true, false, true>(p, st);
+            break;
+        case FwdKind::kDumpInt8FusedQ:
+            causal ? launch_one<D, true, true, true, true>(p, st) : launch_one<D, true, false, true, true>(p, st);
             break;
         case FwdKind::kInt8FusedQ:
             causal ? launch_one<D, true, true, false, true>(p, st) : launch_one<D, true, false, false, true>(p, st);

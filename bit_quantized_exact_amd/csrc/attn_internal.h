@@ -55,7 +55,7 @@ struct FwdParams {
     float* lse;           // fp32 [B,Hq,S] or null
     const float* q_scale; // int8 path: [B,Hq,nqblk]
     const float* k_scale; // int8 path: [B,Hkv,nkblk]
-    int32_t* s_out;       // score dump: [B,Hq,ntiles*BM,S]
+    int32_t* s_out;       // score dump: [B,Hq,ntiles*BM,S] (rows of query tiles tile_lo..)
     float* q_scale_out;   // fused-Q INT8 path: the Q block scales, [B,Hq,nqblk], or null
     const float* v_scale; // 8-bit P.V path: per-channel V scales [B,Hkv,D]
     const int32_t* mask_rowptr;  // tile-mask paths: [nqt + 1] list offsets per query tile
@@ -73,7 +73,9 @@ struct FwdParams {
 // kFp8: E4M3 Q/K codes (v_mfma_f32_32x32x64_f8f6f4), FP16 P.V.
 // kInt8Pv8: INT8 Q/K, E4M3 P and per-channel E4M3 V (transposed tiles).
 // kFp16Mask / kInt8Mask: the FP16 / INT8 forward under a tile-mask list.
-enum class FwdKind { kFp16, kInt8, kDumpInt8, kInt8FusedQ, kFp8, kInt8Pv8, kFp16Mask, kInt8Mask };
+// kDumpInt8 / kDumpInt8FusedQ: the INT8 forward (from INT8 Q, or from fp16 Q
+// quantised in the kernel) writing its INT32 score tiles instead of O.
+enum class FwdKind { kFp16, kInt8, kDumpInt8, kDumpInt8FusedQ, kInt8FusedQ, kFp8, kInt8Pv8, kFp16Mask, kInt8Mask };
 
 int launch_fwd(FwdKind kind, int head_dim, bool causal, const FwdParams& p, hipStream_t st);
 

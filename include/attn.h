@@ -158,17 +158,31 @@ int attn_fwd_fp16(const attn_shape* shape, const void* q_f16, const void* k_f16,
                   const void* v_f16, void* o_f16, float* lse,
                   const int32_t* kv_head_map, int causal, float sm_scale, void* stream);
 
-/* Test hook: the INT32 score tiles of attn_fwd_int8, produced by the same
- * tile code, written out instead of being consumed.  For every (b, h) and
- * every query row i in q-tiles q_tile_lo..q_tile_hi (tiles of BQ rows,
- * inclusive; 0 <= q_tile_lo <= q_tile_hi < ceil(S/BQ), else ATTN_EINVAL),
- * writes S32[i, j] for every visible key
- * j to s_out[b, h, i - q_tile_lo*BQ, j]; s_out is int32
+/* Test hook for [SA] 技术方案's INT8 Q K^T with INT32 accumulation: the INT32
+ * score tiles exactly as attn_fwd_int8 computes them -- the same kernel, with
+ * the same copies of K into LDS, the same LDS layout and the same matrix
+ * instructions, launched on the same work schedule -- written out in place of
+ * the softmax and P V (no V is read).  For every (b, h) and every query row i
+ * in q-tiles q_tile_lo..q_tile_hi (tiles of BQ rows, inclusive;
+ * 0 <= q_tile_lo <= q_tile_hi < ceil(S/BQ), else ATTN_EINVAL), writes
+ * S32[i, j] = sum_c q_i8[b,h,i,c] * k_i8[b,map[h],j,c] for every visible key
+ * j to s_out[b, h, i - q_tile_lo*BQ, j]; s_out is int32 device memory
  * [B, Hq, (q_tile_hi - q_tile_lo + 1) * BQ, S].  Entries of masked keys
  * (j > i when causal) and of rows beyond S are left untouched. */
 int attn_debug_qk_int32(const attn_shape* shape, const int8_t* q_i8, const int8_t* k_i8,
                         const int32_t* kv_head_map, int causal, int32_t q_tile_lo,
                         int32_t q_tile_hi, int32_t* s_out, void* stream);
+
+/* Test hook: as attn_debug_qk_int32, for the kernel of attn_fwd_int8_fused_q,
+ * which reads fp16 Q and quantises each BQ-row block itself ([SA] 技术方案:
+ * per-block INT8 Q).  q_f16 fp16 [B,Hq,S,D]; the scores are those of the INT8
+ * Q codes the kernel forms (the rule of attn_quantize_qk); q_scale_out out
+ * fp32 [B,Hq,ceil(S/BQ)] or NULL receives the Q block scales of the dumped
+ * tiles (other entries untouched).  Same errors as attn_debug_qk_int32. */
+int attn_debug_qk_int32_fused_q(const attn_shape* shape, const void* q_f16, const int8_t* k_i8,
+                                const int32_t* kv_head_map, int causal, int32_t q_tile_lo,
+                                int32_t q_tile_hi, int32_t* s_out, float* q_scale_out,
+                                void* stream);
 
 /* ---- FP8 alternative and 8-bit P.V ablation ------------------------------
  * [SA] 技术方案 chooses INT8 for Q and K because it is more accurate than FP8,

@@ -47,9 +47,9 @@ static void check_shape(int B, int Hq, int S, bool causal, bool dump, int tile_l
     const size_t qk_head_bytes = static_cast<size_t>(S) * St::KROWG;
     const size_t v_head_bytes = static_cast<size_t>(S) * St::VROWG;
     const int nqblk = (S + 127) / 128, nkblk = (S + 63) / 64;
-    // the kernel's item loop: one item per workgroup, or (causal, no dump)
-    // the schedule over the two-items-per-workgroup grid as well
-    const bool persist = causal && !dump;
+    // the kernel's item loop: one item per workgroup, or (causal, the score
+    // dump included) the schedule over the two-items-per-workgroup grid as well
+    const bool persist = causal;
     const int n = static_cast<int>(nblk);
     std::vector<std::pair<int, int>> work;   // (grid, item) in visiting order
     std::vector<char> seen(nblk, 0);
@@ -73,7 +73,7 @@ static void check_shape(int B, int Hq, int S, bool causal, bool dump, int tile_l
     std::fill(seen.begin(), seen.end(), 0);
     for (const auto& w : work) {
         const int item = w.second;
-        const BlockCoord c = decode_item(item, Hq, ntiles, tile_lo, causal && !dump);
+        const BlockCoord c = decode_item(item, Hq, ntiles, tile_lo, causal);
         REQUIRE(c.b >= 0 && c.b < B && c.pos >= 0 && c.pos < Hq && c.qt >= tile_lo &&
                     c.qt < tile_lo + ntiles && c.qt < nqt,
                 "item %d -> b %d pos %d qt %d", item, c.b, c.pos, c.qt);
@@ -127,11 +127,10 @@ static void check_shape(int B, int Hq, int S, bool causal, bool dump, int tile_l
                 for (int j = 0; j < nkt_w; ++j) REQUIRE(j < nkblk, "k scale index %d", j);
             }
         }
-        // staged tiles, in the pipeline order of the kernel
+        // register-staged tiles (the tile-masked kernel's long lists), in the
+        // pipeline order of the kernel
         std::vector<int> kn0, vn0;
-        if (dump) {
-            for (int j = 0; j < nkt; ++j) kn0.push_back(j * kTileN);
-        } else {
+        if (!dump) {
             const int depth = fwd_prefetch_depth(D, INT8);
             for (int t = 0; t <= depth; ++t) kn0.push_back(t * kTileN);
             for (int t = 0; t < depth; ++t) vn0.push_back(t * kTileN);
@@ -141,18 +140,19 @@ static void check_shape(int B, int Hq, int S, bool causal, bool dump, int tile_l
                 vn0.push_back(depth == 2 ? v_load_row<2>(j) : v_load_row<1>(j));
             }
         }
-        // direct-to-LDS staging (all non-dump variants): every (wave,
-        // instruction, lane) slot of every copied tile
-        if (!dump) {
+        // direct-to-LDS staging (every variant; the score dump copies K
+        // tiles only): every (wave, instruction, lane) slot of every copied tile
+        {
             const int nst = (!INT8 && D == 128) ? 2 : 3;
             std::vector<int> dk, dvv;
             for (int t = 0; t < nst; ++t) dk.push_back(t * kTileN);
-            for (int t = 0; t + 1 < nst; ++t) dvv.push_back(t * kTileN);
+            if (!dump)
+                for (int t = 0; t + 1 < nst; ++t) dvv.push_back(t * kTileN);
             const int iters = nst == 2 ? dtl_loop_iterations<2>(nkt) : dtl_loop_iterations<3>(nkt);
             REQUIRE(iters >= nkt && iters % nst == 0, "dtl iterations %d", iters);
             for (int j = 0; j < iters; ++j) {
                 dk.push_back((j + nst) * kTileN);
-                dvv.push_back((j + nst - 1) * kTileN);
+                if (!dump) dvv.push_back((j + nst - 1) * kTileN);
                 const int ks = j + nst < nkblk ? j + nst : nkblk - 1;   // scale ring index, clamped
                 REQUIRE(ks >= 0 && ks < nkblk, "k scale ring %d", ks);
             }

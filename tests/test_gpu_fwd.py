@@ -1,7 +1,11 @@
 """GPU parity of the fused forward kernels against the CPU oracle.
 
-* INT32 score tiles (attn_debug_qk_int32, same tile code as attn_fwd_int8):
-  bit-exact against the oracle's integer scores.
+* INT32 score tiles: bit-exact against the oracle's integer scores, as the
+  INT8 forward kernels compute them -- attn_debug_qk_int32 runs the kernel of
+  attn_fwd_int8 and attn_debug_qk_int32_fused_q that of attn_fwd_int8_fused_q
+  (same copies into LDS, LDS layout, score MFMAs and work schedule), writing
+  the INT32 tiles in place of the softmax; the fused dump's Q block scales
+  are bit-exact too.
 * FP16 path (attn_fwd_fp16): max-abs <= 2e-3 against fp64 exact attention.
 * INT8 path (attn_fwd_int8): cosine >= 0.999 and relative L1 <= 0.02 against
   fp64 exact attention; max-abs <= 2e-3 against the oracle's quantised model
@@ -63,22 +67,39 @@ def _int8_check(w, q, k, v, rows=None, kv_map=None):
 # integer score tiles: bit-exact
 # --------------------------------------------------------------------------
 def _dump_check(w, q, k, tiles, kv_map=None):
+    """Both INT8 kernels' score tiles (INT8 Q from the oracle's quantiser, and
+    fp16 Q quantised in the fused kernel) against the oracle's scores."""
     qz = O.quantize_qk(q, k)
     nqt = -(-w.seq // 128)
+    qd, kd = dev(q), dev(qz["k_i8"])
     for lo, hi in tiles:
         hi = min(hi, nqt - 1)
-        case(f"debug_qk_int32 {w.name} S={w.seq} D={w.head_dim} tiles {lo}..{hi}")
-        s = A.debug_qk_int32(dev(qz["q_i8"]), dev(qz["k_i8"]), causal=w.causal,
-                             kv_head_map=kv_map, tile_lo=lo, tile_hi=hi, fill=-(1 << 31))
-        torch.cuda.synchronize()
-        got = host(s)
         rows = np.arange(lo * 128, min((hi + 1) * 128, w.seq))
         ref = O.scores_i32(qz["q_i8"], qz["k_i8"], causal=w.causal, kv_map=kv_map, rows=rows,
                            fill=-(1 << 31))
-        g = got[:, :, :len(rows)]
-        assert np.array_equal(g, ref), f"{np.count_nonzero(g != ref)} mismatching scores"
-        # rows beyond S stay untouched
-        assert (got[:, :, len(rows):] == -(1 << 31)).all()
+        for fused in (False, True):
+            case(f"debug_qk_int32{'_fused_q' if fused else ''} {w.name} S={w.seq} D={w.head_dim} "
+                 f"causal={w.causal} tiles {lo}..{hi} map={kv_map}")
+            if fused:
+                qs = torch.full(qz["q_scale"].shape, -1.0, dtype=torch.float32, device="cuda")
+                s = A.debug_qk_int32_fused_q(qd, kd, causal=w.causal, kv_head_map=kv_map, tile_lo=lo,
+                                             tile_hi=hi, fill=-(1 << 31), q_scale_out=qs)
+            else:
+                s = A.debug_qk_int32(dev(qz["q_i8"]), kd, causal=w.causal, kv_head_map=kv_map,
+                                     tile_lo=lo, tile_hi=hi, fill=-(1 << 31))
+            torch.cuda.synchronize()
+            got = host(s)
+            g = got[:, :, :len(rows)]
+            assert np.array_equal(g, ref), f"{np.count_nonzero(g != ref)} mismatching scores"
+            # rows beyond S stay untouched
+            assert (got[:, :, len(rows):] == -(1 << 31)).all()
+            del s, got, g
+            if fused:
+                hq = host(qs)
+                assert np.array_equal(hq[:, :, lo:hi + 1], qz["q_scale"][:, :, lo:hi + 1])
+                untouched = np.ones(hq.shape[2], dtype=bool)
+                untouched[lo:hi + 1] = False
+                assert (hq[:, :, untouched] == -1.0).all()
 
 
 @pytest.mark.parametrize("S", [1, 5, 16, 17, 64, 65, 127, 128, 129, 300])
@@ -104,6 +125,20 @@ def test_int32_scores_explicit_map():
     w = small_workload(1, 6, 3, 200, 128, True, seed=77)
     q, k, _ = make_qkv(w)
     _dump_check(w, q, k, [(0, 1)], kv_map=[2, 0, 1, 1, 0, 2])
+    w = small_workload(2, 4, 3, 300, 64, False, seed=78)
+    q, k, _ = make_qkv(w)
+    _dump_check(w, q, k, [(0, 2), (1, 1)], kv_map=[1, 2, 2, 0])
+
+
+@pytest.mark.parametrize("D,Hkv", [(64, 4), (128, 1)])
+def test_int32_scores_two_items_per_workgroup(D, Hkv):
+    """Causal launches with at least 8 work items per compute unit give each
+    workgroup two items (the schedule of the 1024-token batched MQA and the
+    long prefills): every tile of 16 x 16 heads x 1024 tokens, both head dims."""
+    w = small_workload(16, 16, Hkv, 1024, D, True, seed=700 + D)
+    assert 16 * 16 * 8 >= 8 * torch.cuda.get_device_properties(0).multi_processor_count
+    q, k, _ = make_qkv(w)
+    _dump_check(w, q, k, [(0, 7)])
 
 
 # --------------------------------------------------------------------------
@@ -333,7 +368,7 @@ def test_fused_q_matches_two_call_path_bitwise(S, D, Hq, Hkv, causal):
     assert torch.equal(lse, lse_ref)
 
 
-@pytest.mark.parametrize("name", ["llm_prefill_gqa", "batched_mqa", "video_mha"])
+@pytest.mark.parametrize("name", ["llm_prefill_gqa", "batched_mqa", "video_mha", "long_gqa"])
 def test_fused_q_workloads_bitwise_and_accuracy(name):
     w = WORKLOADS[name]
     q, k, v = make_qkv(w)
