@@ -21,11 +21,11 @@ ATTN_MAX_SEQ = 1 << 22
 EXPORTED = (
     "attn_quant_blocks", "attn_quantize_workspace_bytes", "attn_quantize_qk", "attn_quantize_k",
     "attn_fwd_int8", "attn_fwd_int8_fused_q", "attn_fwd_fp16", "attn_debug_qk_int32",
+    "attn_debug_qk_int32_fused_q",
     "attn_status_string", "attn_quantize_qk_fp8", "attn_fwd_fp8", "attn_v_fp8_stride",
     "attn_quantize_v_fp8", "attn_fwd_int8_pv8", "attn_decode_workspace_bytes", "attn_decode_int8",
     "attn_decode_fp16", "attn_block_mask_tiles", "attn_block_mask_apb", "attn_block_mask_csr",
     "attn_fwd_fp16_masked", "attn_fwd_int8_masked",
-    "attn_probe_mfma", "attn_probe_compute_units",
 )
 
 
@@ -74,6 +74,8 @@ def lib():
     L.attn_fwd_fp16.restype = ctypes.c_int
     L.attn_debug_qk_int32.argtypes = [SP, P, P, P, ctypes.c_int, I32, I32, P, P]
     L.attn_debug_qk_int32.restype = ctypes.c_int
+    L.attn_debug_qk_int32_fused_q.argtypes = [SP, P, P, P, ctypes.c_int, I32, I32, P, P, P]
+    L.attn_debug_qk_int32_fused_q.restype = ctypes.c_int
     L.attn_quantize_qk_fp8.argtypes = [SP, P, P, P, P, P, P, P, P, P]
     L.attn_quantize_qk_fp8.restype = ctypes.c_int
     L.attn_fwd_fp8.argtypes = [SP, P, P, P, P, P, P, P, P, ctypes.c_int, F32, P]
@@ -103,9 +105,5 @@ def lib():
     L.attn_fwd_int8_masked.restype = ctypes.c_int
     L.attn_status_string.argtypes = [ctypes.c_int]
     L.attn_status_string.restype = ctypes.c_char_p
-    L.attn_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, ctypes.POINTER(ctypes.c_double), P]
-    L.attn_probe_mfma.restype = ctypes.c_int
-    L.attn_probe_compute_units.argtypes = [ctypes.POINTER(ctypes.c_int)]
-    L.attn_probe_compute_units.restype = ctypes.c_int
     _lib = L
     return L

@@ -1,12 +1,13 @@
 /*
- * attn_probe.h - measurement helpers exported by libattn.so beside the
- * attention calls of attn.h.  They are not part of the attention path: the
- * benchmark uses them to report the sustained matrix-core rate of the device
- * next to the published peaks, so that a kernel's fraction of the peak can be
- * read against what a dense MFMA loop reaches on the same part.
+ * mfma_probe.h - measurement helpers of libattn_probe.so, a small library
+ * of its own beside libattn.so.  They are not part of the attention path and
+ * not part of its C ABI: the benchmark uses them to report the sustained
+ * matrix-core rate of the device next to the published peaks, so that a
+ * kernel's fraction of the peak can be read against what a dense MFMA loop
+ * reaches on the same part.
  */
-#ifndef ATTN_PROBE_H
-#define ATTN_PROBE_H
+#ifndef ATTN_MFMA_PROBE_H
+#define ATTN_MFMA_PROBE_H
 
 #ifdef __cplusplus
 extern "C" {
@@ -33,4 +34,4 @@ int attn_probe_compute_units(int* cus);
 }
 #endif
 
-#endif /* ATTN_PROBE_H */
+#endif /* ATTN_MFMA_PROBE_H */

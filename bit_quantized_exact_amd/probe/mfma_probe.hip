@@ -8,7 +8,7 @@
 // accumulators are summed into one value per lane at the end (so the loop is
 // not removed).  Two 256-thread workgroups per compute unit give two waves
 // per SIMD, as in the forward kernels.
-#include "attn_probe.h"
+#include "mfma_probe.h"
 
 #include <hip/hip_runtime.h>
 

@@ -1,7 +1,8 @@
 """C-ABI checks that need no GPU: the library loads, exports every symbol that
-include/attn.h and include/attn_probe.h declare, and rejects every invalid
-argument on the host, before any HIP call (each call below fails validation,
-so nothing launches)."""
+include/attn.h declares, and rejects every invalid argument on the host,
+before any HIP call (each call below fails validation, so nothing launches).
+The Python wrappers' own checks (buffer shapes, devices, the length of the
+kv-head map) are tested here too, on CPU tensors."""
 import ctypes
 import os
 import re
@@ -16,13 +17,15 @@ FAKE = 0x10000          # 16-byte aligned, never dereferenced: validation fails 
 MISALIGNED = 0x10008
 
 
-def _declared():
-    names = set()
-    for h in ("attn.h", "attn_probe.h"):
-        text = open(os.path.join(ROOT, "include", h)).read()
-        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-        names |= set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text))
-    return sorted(names)
+def _declared(path=os.path.join(ROOT, "include", "attn.h")):
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_public_header_is_checked():
+    """include/ holds the ABI of libattn.so only."""
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == ["attn.h"]
 
 
 def test_header_and_binding_agree():
@@ -153,11 +156,70 @@ def test_debug_tile_range(lo, hi):
     assert L.attn_debug_qk_int32(ctypes.byref(sh), FAKE, FAKE, None, 0, lo, hi, FAKE, None) == -1
 
 
+@pytest.mark.parametrize("lo,hi", [(-1, 0), (1, 0), (0, 2), (2, 2)])
+def test_debug_fused_q_tile_range(lo, hi):
+    L = A.lib()
+    sh = _sh(S=256)    # two query tiles
+    assert L.attn_debug_qk_int32_fused_q(ctypes.byref(sh), FAKE, FAKE, None, 0, lo, hi, FAKE, None, None) == -1
+
+
 def test_debug_null_and_alignment():
     L = A.lib()
     sh = _sh()
     assert L.attn_debug_qk_int32(ctypes.byref(sh), None, FAKE, None, 0, 0, 0, FAKE, None) == -1
     assert L.attn_debug_qk_int32(ctypes.byref(sh), FAKE, FAKE, None, 0, 0, 0, FAKE + 2, None) == -1
+    F = L.attn_debug_qk_int32_fused_q
+    assert F(None, FAKE, FAKE, None, 0, 0, 0, FAKE, None, None) == -1
+    assert F(ctypes.byref(sh), None, FAKE, None, 0, 0, 0, FAKE, None, None) == -1
+    assert F(ctypes.byref(sh), FAKE, None, None, 0, 0, 0, FAKE, None, None) == -1
+    assert F(ctypes.byref(sh), FAKE, FAKE, None, 0, 0, 0, None, None, None) == -1
+    assert F(ctypes.byref(sh), MISALIGNED, FAKE, None, 0, 0, 0, FAKE, None, None) == -1
+    assert F(ctypes.byref(sh), FAKE, FAKE, None, 0, 0, 0, FAKE, FAKE + 2, None) == -1
+    bad = (ctypes.c_int32 * 4)(0, 1, 2, 0)
+    assert F(ctypes.byref(sh), FAKE, FAKE, ctypes.cast(bad, ctypes.c_void_p), 0, 0, 0, FAKE, None, None) == -4
+    assert F(ctypes.byref(_sh(D=96)), FAKE, FAKE, None, 0, 0, 0, FAKE, None, None) == -2
+
+
+# --------------------------------------------------------------------------
+# the Python wrappers' own checks (CPU tensors stand in for device buffers)
+# --------------------------------------------------------------------------
+def test_map_arg_requires_one_entry_per_query_head():
+    arr, ptr = A._map_arg([0, 1, 1, 0], 4)
+    assert list(arr) == [0, 1, 1, 0] and ptr is not None
+    assert A._map_arg(None, 4) == (None, None)
+    for bad in ([0, 1, 1], [0, 1, 1, 0, 1], []):
+        with pytest.raises(ValueError):
+            A._map_arg(bad, 4)
+
+
+def test_buffer_checks_reject_wrong_shape_dtype_device_layout():
+    import torch
+    cpu = torch.device("cpu")
+    good = torch.zeros(1, 4, 256, 128, dtype=torch.float16)
+    assert A._out_arg(good, (1, 4, 256, 128), cpu) is good
+    for bad in (torch.zeros(1, 4, 255, 128, dtype=torch.float16),          # short
+                torch.zeros(1, 4, 256, 128, dtype=torch.float32),          # dtype
+                torch.zeros(1, 4, 128, 256, dtype=torch.float16).transpose(2, 3)):   # layout
+        with pytest.raises(ValueError):
+            A._out_arg(bad, (1, 4, 256, 128), cpu)
+    with pytest.raises(ValueError):
+        A._out_arg(good, (1, 4, 256, 128), torch.device("meta"))           # device
+    lse = torch.zeros(1, 4, 256, dtype=torch.float32)
+    assert A._lse_arg(lse, False, (1, 4, 256), cpu) is lse
+    assert A._lse_arg(None, False, (1, 4, 256), cpu) is None
+    assert A._lse_arg(None, True, (1, 4, 256), cpu).shape == (1, 4, 256)
+    for bad in (torch.zeros(1, 4, 256, dtype=torch.float16), torch.zeros(1, 4, 200, dtype=torch.float32),
+                torch.zeros(4, 256, dtype=torch.float32)):
+        with pytest.raises(ValueError):
+            A._lse_arg(bad, True, (1, 4, 256), cpu)
+    qs = torch.zeros(1, 4, 3, dtype=torch.float32)          # ceil(300 / 128) blocks
+    assert A._scales(qs, 1, 4, 300, 128, cpu, "q_scale") is qs
+    for bad in (torch.zeros(1, 4, 2, dtype=torch.float32), torch.zeros(1, 2, 3, dtype=torch.float32),
+                torch.zeros(1, 4, 3, dtype=torch.float64)):
+        with pytest.raises(ValueError):
+            A._scales(bad, 1, 4, 300, 128, cpu, "q_scale")
+    with pytest.raises(ValueError):
+        A._same_device(good, torch.zeros(1, device="meta"))
 
 
 def test_python_binding_rejects_cpu_tensors():
@@ -312,8 +374,20 @@ def test_decode_workspace_and_validation():
                               None) == -1
 
 
+def test_mfma_probe_library_is_separate():
+    """The dense MFMA loop lives in libattn_probe.so, not in the attention ABI."""
+    from bit_quantized_exact_amd import probe
+    hdr = os.path.join(ROOT, "bit_quantized_exact_amd", "probe", "mfma_probe.h")
+    assert _declared(hdr) == sorted(probe.EXPORTED)
+    L = probe.lib()
+    for name in probe.EXPORTED:
+        assert hasattr(L, name)
+        assert not hasattr(A.lib(), name)
+
+
 def test_mfma_probe_rejects_bad_arguments():
-    L = A.lib()
+    from bit_quantized_exact_amd import probe
+    L = probe.lib()
     ops = ctypes.c_double(0.0)
     assert L.attn_probe_mfma(4, 1, 1, FAKE, ctypes.byref(ops), None) == -1    # unknown kind
     assert L.attn_probe_mfma(-1, 1, 1, FAKE, ctypes.byref(ops), None) == -1   # unknown kind
