@@ -1,42 +1,45 @@
 """Benchmark of the attention forward hot path on one MI355X.
 
-One step = one pass of the whole hot path over the LLM-prefill workload
-(batch 1, 32 query heads / 8 kv heads, seq 8192, head_dim 128, causal GQA,
-synthetic fp16 inputs already resident in HBM):
+One step = one pass of the whole hot path over the long-context GQA workload
+(batch 1, 32 query heads / 8 kv heads, seq 32768, head_dim 128, causal GQA,
+synthetic fp16 inputs already resident in HBM; the largest of the five
+workloads, 8.8 TFLOP per attention call):
     attn_quantize_k        (K channel mean, smoothing, per-block INT8 K)
     attn_fwd_int8_fused_q  (per-block INT8 Q in the kernel, INT8 QK^T,
                             online softmax, FP16 P.V)
     attn_fwd_fp16          (the exact FP16 FlashAttention-style baseline)
-Outside the timed steps it also times the FP8 alternative (attn_quantize_qk_fp8
-+ attn_fwd_fp8) and the 8-bit P.V ablation (attn_quantize_v_fp8 +
-attn_fwd_int8_pv8) and, with the CPU leg, reports their accuracy against the
-exact oracle on the sampled rows; and the KV-cache decode kernels
-(attn_decode_int8, attn_decode_fp16) on the decode workload (batch 16, one
-query per sequence over an 8192-token cache), as GB/s against HBM; and the
-tile-masked forwards under the APB layout of the same prefill shape (1024
-anchor, 2048 passing, 5120 local tokens), FLOP over the visible pairs.
 
 Printed: ONE JSON line.  `value` is the INT8 (SageAttention-form) path's
 attention throughput, quantisation included: FLOP / (t_quantize_k +
 t_fwd_int8_fused_q), with FLOP = 4*B*Hq*S^2*D/2 (causal) and the per-call
 times taken with HIP events on the launch stream inside the timed steps.  The
-FP16 path, the INT8 forward alone and (outside the timed steps) the two-call
-INT8 path attn_quantize_qk + attn_fwd_int8 are reported beside it, each as
-TFLOPS and as a fraction of MI355X's published dense MFMA peak (fp16
-2.5 PFLOP/s, int8 5.0 POP/s).
+FP16 path and the INT8 forward alone are reported beside it, each as TFLOPS and
+as a fraction of MI355X's published dense MFMA peak (fp16 2.5 PFLOP/s, int8
+5.0 POP/s, and for the INT8 path the harmonic blend of the two, its QK^T half
+running at the INT8 rate and its P.V half at the FP16 rate).
+
+`paths.configs` times the same three calls on each of the five workloads (the
+tiny MHA, the 8192-token LLM prefill, the video-diffusion MHA, the long GQA
+and the batched MQA) in the same process.  Outside the timed steps the line
+also carries, on the headline workload, the two-call INT8 path
+(attn_quantize_qk + attn_fwd_int8), the FP8 alternative and the 8-bit P.V
+ablation; the KV-cache decode kernels (batch 16, one query over an 8192-token
+cache) as GB/s against HBM; and the tile-masked forwards under the APB layout
+of the 8192-token prefill (1024 anchor, 2048 passing, 5120 local tokens).
 
 `roofline` describes the dominant kernel of the step; `mfma_loop` gives, as
 context for its published peak, the rate a dense MFMA loop sustains on this
-device (attn_probe_mfma); `cpu_baseline` times the CPU oracle (fp64, plain
-loops) on a bounded sample of the same workload's query rows, on this
-machine's host cores.
+device (libattn_probe.so); `cpu_baseline` times the CPU oracle (fp64, plain
+loops) on a bounded, seeded sample of the headline workload's query rows, on
+this machine's host cores, and `parity_sample` compares the GPU outputs with
+it on those rows.
 
 Each timed section is preceded by untimed calls for CLOCK_WARM_MS of busy
 time (the clocks ramp up after the GPU idled while the CPU drew the inputs),
 then the W warm-up steps, then exactly K timed steps.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-       [--all-workloads] [--no-cpu] [--clock-warm-ms MS]
+       [--no-configs] [--no-cpu] [--clock-warm-ms MS]
        python bench.py --decode-only [--decode-reps N]      (profiling)
        python bench.py --copy-calibration BYTES             (HBM counter scale)
 """
@@ -58,7 +61,8 @@ sys.path.insert(0, ROOT)
 PEAK_TFLOPS = {"fp16": 2500.0, "int8": 5000.0}
 PEAK_BLEND = 2.0 / (1.0 / PEAK_TFLOPS["int8"] + 1.0 / PEAK_TFLOPS["fp16"])
 HBM_PEAK_GBS = 8000.0
-DEFAULT_WORKLOAD = "llm_prefill_gqa"
+DEFAULT_WORKLOAD = "long_gqa"
+APB_WORKLOAD = "llm_prefill_gqa"
 
 
 def parse():
@@ -67,8 +71,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--all-workloads", action="store_true",
-                    help="one JSON line per workload (no CPU baseline)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload block paths.configs")
+    ap.add_argument("--config-steps", type=int, default=10,
+                    help="timed steps per workload in paths.configs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -134,16 +140,36 @@ def clock_warm(fn, min_ms=None, batch=4):
             return n
 
 
-def run_workload(name, steps, warmup, cpu=False, cpu_seconds=15.0):
+def algorithmic_bytes(w):
+    """Bytes each call must move (every tensor read or written once)."""
+    B, Hq, Hkv, S, D = w.batch, w.heads_q, w.heads_kv, w.seq, w.head_dim
+    nq, nk = B * Hq * S * D, B * Hkv * S * D
+    kscales = 4 * B * Hkv * math.ceil(S / 64)
+    return {
+        "fwd_fp16": 2 * (2 * nq + 2 * nk),                       # Q, K, V read; O written
+        "fwd_int8": 2 * nq + nk + 2 * nk + 2 * nq + kscales,     # fp16 Q, int8 K, fp16 V, O, K scales
+        "quantize_k": 2 * 2 * nk + nk + kscales,                 # K read twice, int8 K and scales written
+    }
+
+
+def time_core(w, steps, warmup, tensors=None):
+    """Times the step's three calls (attn_quantize_k, attn_fwd_int8_fused_q,
+    attn_fwd_fp16) on workload w with HIP events on the launch stream: a clock
+    warm-up, `warmup` untimed steps, then `steps` timed ones.  Returns the mean
+    per-call milliseconds, the wall time of the timed steps and the device
+    tensors (inputs and outputs)."""
     import torch
 
     import bit_quantized_exact_amd as A
-    from bit_quantized_exact_amd.inputs import WORKLOADS, make_qkv
+    from bit_quantized_exact_amd.inputs import make_qkv
 
-    w = WORKLOADS[name]
-    q, k, v = make_qkv(w)
-    dev = torch.device("cuda:0")
-    qd, kd, vd = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+    if tensors is None:
+        q, k, v = make_qkv(w)
+        dev = torch.device("cuda:0")
+        qd, kd, vd = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+        del q, k, v
+    else:
+        qd, kd, vd = tensors
     # outputs and workspace allocated once: the timed steps only launch kernels
     kz = A.quantize_k(kd, with_mean=False)
     o8 = torch.empty_like(qd)
@@ -175,11 +201,51 @@ def run_workload(name, steps, warmup, cpu=False, cpu_seconds=15.0):
         step(ev[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    mean = lambda a, b: float(np.mean([e[a].elapsed_time(e[b]) for e in ev]))
+    return dict(ms_q=mean(0, 1), ms_8=mean(1, 2), ms_16=mean(2, 3), wall=wall, prewarm=prewarm_calls,
+                qd=qd, kd=kd, vd=vd, kz=kz, o8=o8, o16=o16)
 
-    t_q = np.array([e[0].elapsed_time(e[1]) for e in ev])
-    t_8 = np.array([e[1].elapsed_time(e[2]) for e in ev])
-    t_16 = np.array([e[2].elapsed_time(e[3]) for e in ev])
-    ms_q, ms_8, ms_16 = float(t_q.mean()), float(t_8.mean()), float(t_16.mean())
+
+def config_entry(w, t):
+    """The per-workload record of paths.configs."""
+    flop = w.flops()
+    tf = lambda ms: flop / (ms * 1e-3) / 1e12
+    by = algorithmic_bytes(w)
+    e2e = tf(t["ms_q"] + t["ms_8"])
+    return {
+        "shape": {"batch": w.batch, "heads_q": w.heads_q, "heads_kv": w.heads_kv, "seq": w.seq,
+                  "head_dim": w.head_dim, "causal": w.causal},
+        "flop": flop,
+        "int8": {"tflops": round(e2e, 2), "ms": round(t["ms_q"] + t["ms_8"], 4),
+                 "frac_int8_peak": round(e2e / PEAK_TFLOPS["int8"], 4),
+                 "frac_blended_peak": round(e2e / PEAK_BLEND, 4)},
+        "int8_fwd_only": {"tflops": round(tf(t["ms_8"]), 2), "ms": round(t["ms_8"], 4),
+                          "frac_int8_peak": round(tf(t["ms_8"]) / PEAK_TFLOPS["int8"], 4),
+                          "frac_blended_peak": round(tf(t["ms_8"]) / PEAK_BLEND, 4)},
+        "fp16": {"tflops": round(tf(t["ms_16"]), 2), "ms": round(t["ms_16"], 4),
+                 "frac_fp16_peak": round(tf(t["ms_16"]) / PEAK_TFLOPS["fp16"], 4)},
+        "quantize_k": {"ms": round(t["ms_q"], 4),
+                       "gbs": round(by["quantize_k"] / (t["ms_q"] * 1e-3) / 1e9, 1),
+                       "frac_hbm_peak": round(by["quantize_k"] / (t["ms_q"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "int8_speedup_over_fp16": round(t["ms_16"] / (t["ms_q"] + t["ms_8"]), 3),
+    }
+
+
+def run_workload(name, steps, warmup, cpu=False, cpu_seconds=15.0, configs=True, config_steps=10):
+    import torch
+
+    import bit_quantized_exact_amd as A
+    from bit_quantized_exact_amd.inputs import WORKLOADS, make_qkv
+
+    w = WORKLOADS[name]
+    q, k, v = make_qkv(w)
+    dev = torch.device("cuda:0")
+    t = time_core(w, steps, warmup, tensors=tuple(torch.from_numpy(x).to(dev) for x in (q, k, v)))
+    if not cpu:
+        del q, k, v
+    qd, kd, vd, o8, o16 = t["qd"], t["kd"], t["vd"], t["o8"], t["o16"]
+    ms_q, ms_8, ms_16, wall = t["ms_q"], t["ms_8"], t["ms_16"], t["wall"]
+    stream = torch.cuda.current_stream()
 
     # the two-call INT8 path (separate Q quantisation), timed after the steps
     qz = A.quantize_qk(qd, kd, with_mean=False)
@@ -227,28 +293,22 @@ def run_workload(name, steps, warmup, cpu=False, cpu_seconds=15.0):
     A.fwd_fp8(qz8, vd, causal=w.causal, out=of8)
     A.quantize_v_fp8(vd, workspace=vz8["workspace"])
     A.fwd_int8_pv8(qz, vz8, causal=w.causal, out=opv8)
-    A.fwd_int8_fused_q(qd, kz, vd, causal=w.causal, out=o8)   # o8 is compared below
+    A.fwd_int8_fused_q(qd, t["kz"], vd, causal=w.causal, out=o8)   # o8 is compared below
+    del qz8, vz8, qz
     flop = w.flops()
     tf = lambda ms: flop / (ms * 1e-3) / 1e12
     int8_e2e = tf(ms_q + ms_8)
-
-    # algorithmic bytes (each tensor read or written once)
-    B, Hq, Hkv, S, D = w.batch, w.heads_q, w.heads_kv, w.seq, w.head_dim
-    nq, nk = B * Hq * S * D, B * Hkv * S * D
-    bytes_fp16 = 2 * (2 * nq + 2 * nk)                      # Q, K, V read; O written
-    # fused INT8 forward: fp16 Q, int8 K, fp16 V read; O written (+ K scales)
-    bytes_int8 = 2 * nq + nk + 2 * nk + 2 * nq + 4 * B * Hkv * math.ceil(S / 64)
-    bytes_quant = 2 * 2 * nk + nk                           # K twice (sum + quantise), int8 K out
+    by = algorithmic_bytes(w)
 
     kernels = {
-        "fwd_fp16": dict(ms=ms_16, flop=flop, peak=PEAK_TFLOPS["fp16"], bytes=bytes_fp16),
-        "fwd_int8": dict(ms=ms_8, flop=flop, peak=PEAK_BLEND, bytes=bytes_int8),
-        "quantize_qk": dict(ms=ms_q, flop=0.0, peak=None, bytes=bytes_quant),
+        "fwd_fp16": dict(ms=ms_16, peak=PEAK_TFLOPS["fp16"]),
+        "fwd_int8": dict(ms=ms_8, peak=PEAK_BLEND),
+        "quantize_k": dict(ms=ms_q, peak=None),
     }
     dom = max(kernels, key=lambda n: kernels[n]["ms"])
     kd_ = kernels[dom]
-    if dom == "quantize_qk":
-        achieved = kd_["bytes"] / (kd_["ms"] * 1e-3) / 1e9
+    if dom == "quantize_k":
+        achieved = by[dom] / (kd_["ms"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS}
     elif dom == "fwd_fp16":
@@ -261,9 +321,12 @@ def run_workload(name, steps, warmup, cpu=False, cpu_seconds=15.0):
                 "unit": "TFLOP/s", "frac": achieved / PEAK_BLEND,
                 "peak_note": "int8 QK^T at 5.0 POP/s and fp16 PV at 2.5 PFLOP/s, harmonic blend"}
     roof["kernel"] = {"fwd_fp16": "attn_fwd_fp16", "fwd_int8": "attn_fwd_int8_fused_q",
-                      "quantize_qk": "attn_quantize_k"}[dom]
+                      "quantize_k": "attn_quantize_k"}[dom]
     roof["traffic"] = counters_for(dom, name)
+    roof["algorithmic_bytes"] = by[dom]
+    roof["flop_per_launch"] = flop if dom != "quantize_k" else 0.0
 
+    B, Hq, Hkv, S, D = w.batch, w.heads_q, w.heads_kv, w.seq, w.head_dim
     rec = {
         "metric": "attention fwd TFLOPS (INT8 & FP16 paths) and % of gfx950 MFMA peak, 1 GPU",
         "value": round(int8_e2e, 2),
@@ -271,7 +334,7 @@ def run_workload(name, steps, warmup, cpu=False, cpu_seconds=15.0):
         "n_gpus": 1,
         "steps": steps,
         "warmup": warmup,
-        "clock_warmup": {"ms": CLOCK_WARM_MS, "steps": prewarm_calls,
+        "clock_warmup": {"ms": CLOCK_WARM_MS, "steps": t["prewarm"],
                          "note": "untimed steps before the warm-up steps, until the clocks have ramped"},
         "ms_per_step": round(wall / steps * 1e3, 4),
         "higher_is_better": True,
@@ -286,13 +349,17 @@ def run_workload(name, steps, warmup, cpu=False, cpu_seconds=15.0):
             "int8": {"tflops": round(int8_e2e, 2), "ms": round(ms_q + ms_8, 4),
                      "fwd_only_tflops": round(tf(ms_8), 2), "fwd_ms": round(ms_8, 4),
                      "quantize_ms": round(ms_q, 4),
-                     "quantize_gbs": round(bytes_quant / (ms_q * 1e-3) / 1e9, 1),
+                     "quantize_gbs": round(by["quantize_k"] / (ms_q * 1e-3) / 1e9, 1),
+                     "quantize_frac_hbm_peak": round(by["quantize_k"] / (ms_q * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "two_call_tflops": round(tf(ms_qqk + ms_8u), 2),
                      "two_call_quantize_qk_ms": round(ms_qqk, 4),
                      "two_call_fwd_int8_ms": round(ms_8u, 4),
-                     "frac_int8_peak": round(tf(ms_q + ms_8) / PEAK_TFLOPS["int8"], 4),
-                     "frac_blended_peak": round(tf(ms_q + ms_8) / PEAK_BLEND, 4),
-                     "fwd_only_frac_blended_peak": round(tf(ms_8) / PEAK_BLEND, 4)},
+                     "frac_int8_peak": round(int8_e2e / PEAK_TFLOPS["int8"], 4),
+                     "frac_blended_peak": round(int8_e2e / PEAK_BLEND, 4),
+                     "fwd_only_frac_blended_peak": round(tf(ms_8) / PEAK_BLEND, 4),
+                     "fwd_traffic": counters_for("fwd_int8", name),
+                     "fwd_algorithmic_bytes": by["fwd_int8"],
+                     "quantize_traffic": counters_for("quantize_k", name)},
             "fp16": {"tflops": round(tf(ms_16), 2), "ms": round(ms_16, 4),
                      "frac_fp16_peak": round(tf(ms_16) / PEAK_TFLOPS["fp16"], 4)},
             "int8_speedup_over_fp16": round(ms_16 / (ms_q + ms_8), 3),
@@ -309,13 +376,28 @@ def run_workload(name, steps, warmup, cpu=False, cpu_seconds=15.0):
         "roofline": {k_: (round(v_, 4) if isinstance(v_, float) else v_) for k_, v_ in roof.items()},
         "cpu_baseline": None,
     }
-    rec["paths"]["decode"] = run_decode()
-    if name == DEFAULT_WORKLOAD:
-        rec["paths"]["apb_masked"] = run_apb(qd, kd, vd, qz, w)
-        rec["mfma_loop"] = run_mfma_loop()
     if cpu:
         rec["cpu_baseline"], rec["parity_sample"] = cpu_baseline(w, q, k, v, o8, o16, cpu_seconds,
                                                                  extra={"fp8_qk": of8, "int8_pv8": opv8})
+        del q, k, v
+    del of8, opv8
+    own = config_entry(w, t)
+    del t, qd, kd, vd, o8, o16
+    torch.cuda.empty_cache()
+    if configs:
+        rec["paths"]["configs"] = {}
+        for cname, cw in WORKLOADS.items():
+            if cname == name:
+                rec["paths"]["configs"][cname] = dict(own, timed_steps=steps, note="the headline steps")
+                continue
+            ct = time_core(cw, config_steps, max(1, warmup // 2))
+            rec["paths"]["configs"][cname] = dict(config_entry(cw, ct), timed_steps=config_steps)
+            if cname == APB_WORKLOAD:
+                rec["paths"]["apb_masked"] = run_apb(ct["qd"], ct["kd"], ct["vd"], cw)
+            del ct
+            torch.cuda.empty_cache()
+    rec["paths"]["decode"] = run_decode()
+    rec["mfma_loop"] = run_mfma_loop()
     return rec
 
 
@@ -332,9 +414,9 @@ def run_mfma_loop(iters=20000, reps=5):
 
     import torch
 
-    import bit_quantized_exact_amd as A
+    from bit_quantized_exact_amd import probe
 
-    L = A.lib()
+    L = probe.lib()
     cus = ctypes.c_int(0)
     if L.attn_probe_compute_units(ctypes.byref(cus)) != 0 or cus.value <= 0:
         return None
@@ -425,13 +507,14 @@ def run_decode(name="decode_gqa", reps=20, warm_ms=None):
     return out
 
 
-def run_apb(qd, kd, vd, qz, w, anchor=1024, passing=2048, reps=10):
+def run_apb(qd, kd, vd, w, anchor=1024, passing=2048, reps=10):
     """The LLM-prefill shape under the APB tile mask (keys [anchor | passing |
     local]): the FP16 and INT8 masked forwards; FLOP over the visible pairs."""
     import torch
 
     import bit_quantized_exact_amd as A
 
+    qz = A.quantize_qk(qd, kd, with_mean=False)
     S = w.seq
     csr = A.block_mask_csr(S, A.apb_block_mask(S, anchor, passing))
     o = torch.empty_like(qd)
@@ -450,7 +533,8 @@ def run_apb(qd, kd, vd, qz, w, anchor=1024, passing=2048, reps=10):
     rows = np.r_[0:anchor, anchor + passing:S]
     pairs = float((rows + 1).sum())
     flop = 4.0 * w.batch * w.heads_q * w.head_dim * pairs
-    out = {"anchor": anchor, "passing": passing, "local": S - anchor - passing, "mask_tiles_listed": csr["nnz"]}
+    out = {"workload": w.name, "anchor": anchor, "passing": passing, "local": S - anchor - passing,
+           "mask_tiles_listed": csr["nnz"]}
     for tag in ("fp16", "int8"):
         out[tag] = {"ms": round(res[tag], 4), "tflops": round(flop / (res[tag] * 1e-3) / 1e12, 2)}
     return out
@@ -502,6 +586,8 @@ def cpu_baseline(w, q, k, v, o8, o16, target_s, extra=None):
                    f"{w.batch * w.heads_q} (batch, head) pairs; fp64 exact attention; "
                    f"{fl / 1e9:.1f} GFLOP in {dt:.2f} s"),
         "seconds": round(dt, 3),
+        "full_workload_seconds_extrapolated": round(w.flops() / (fl / dt), 1),
+        "extrapolation_note": "the whole workload's oracle time at the sample's rate (extrapolated, not run)",
     }
     return base, parity
 
@@ -534,13 +620,9 @@ def main():
     if args.decode_only:
         print(json.dumps(run_decode(reps=args.decode_reps)), flush=True)
         return
-    if args.all_workloads:
-        from bit_quantized_exact_amd.inputs import WORKLOADS
-        for name in WORKLOADS:
-            print(json.dumps(run_workload(name, args.steps, args.warmup)), flush=True)
-        return
     rec = run_workload(args.workload, args.steps, args.warmup, cpu=not args.no_cpu,
-                       cpu_seconds=args.cpu_seconds)
+                       cpu_seconds=args.cpu_seconds, configs=not args.no_configs,
+                       config_steps=args.config_steps)
     print(json.dumps(rec), flush=True)
 
 
