@@ -7,6 +7,7 @@ kernels.  torch provides device memory and streams.
 
     attn_quantize_qk -> quantize_qk     K smoothing + per-block INT8 Q/K
     attn_quantize_k  -> quantize_k      K smoothing + per-block INT8 K only
+    attn_quantize_k_noalloc -> quantize_k_noalloc   the same, workspace from the library's scratch
     attn_fwd_int8    -> fwd_int8        INT8 QK^T, FP16 PV, online softmax
     attn_fwd_int8_fused_q -> fwd_int8_fused_q   the same, quantising Q in the kernel
     attn_fwd_fp16    -> fwd_fp16        exact FP16 FlashAttention-style forward
@@ -37,7 +38,7 @@ from . import _native
 from ._native import AttnKvShape, AttnShape, lib
 
 __all__ = [
-    "AttnError", "quant_blocks", "quantize_workspace_bytes", "quantize_qk", "quantize_k",
+    "AttnError", "quant_blocks", "quantize_workspace_bytes", "quantize_qk", "quantize_k", "quantize_k_noalloc",
     "fwd_int8", "fwd_int8_fused_q", "fwd_fp16", "debug_qk_int32", "debug_qk_int32_fused_q", "sageattn",
     "status_string",
     "quantize_qk_fp8", "fwd_fp8", "v_fp8_stride", "quantize_v_fp8", "fwd_int8_pv8",
@@ -222,6 +223,24 @@ def quantize_k(k: torch.Tensor, *, out: Optional[dict] = None,
     _check(lib().attn_quantize_k(ctypes.byref(sh), _ptr(k), _ptr(o["k_i8"]), _ptr(o["k_scale"]),
                                  _ptr(o["k_mean"]), _ptr(workspace), _stream(stream)),
            "attn_quantize_k")
+    return o
+
+
+def quantize_k_noalloc(k: torch.Tensor, *, out: Optional[dict] = None, with_mean: bool = True, stream=None):
+    """quantize_k whose workspace is the library's own device scratch
+    (attn_quantize_k_noalloc): the C call allocates nothing; outputs not
+    given in `out` are allocated here by torch.  Calls that overlap on one
+    GPU share the scratch and race."""
+    _dev(k, torch.float16, "k")
+    if k.dim() != 4:
+        raise ValueError("k must be [batch, heads, seq, head_dim]")
+    B, Hkv, S, D = k.shape
+    sh = AttnShape(B, Hkv, Hkv, S, D)
+    o = _quant_outputs(dict(out) if out is not None else {}, sh, k.device, False, with_mean)
+    o.pop("workspace", None)
+    _check(lib().attn_quantize_k_noalloc(ctypes.byref(sh), _ptr(k), _ptr(o["k_i8"]), _ptr(o["k_scale"]),
+                                         _ptr(o["k_mean"]), _stream(stream)),
+           "attn_quantize_k_noalloc")
     return o
 
 

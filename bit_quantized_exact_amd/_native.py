@@ -14,12 +14,14 @@ import torch  # noqa: F401  (must load before libattn.so, see above)
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libattn.so")
 
-ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_ELAUNCH, ATTN_ERANGE = 0, -1, -2, -3, -4
+ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_ELAUNCH, ATTN_ERANGE, ATTN_ESCRATCH = 0, -1, -2, -3, -4, -5
+ATTN_NOALLOC_SCRATCH_BYTES = 16 << 20
 ATTN_MAX_HEADS = 256
 ATTN_MAX_SEQ = 1 << 22
 
 EXPORTED = (
     "attn_quant_blocks", "attn_quantize_workspace_bytes", "attn_quantize_qk", "attn_quantize_k",
+    "attn_quantize_k_noalloc",
     "attn_fwd_int8", "attn_fwd_int8_fused_q", "attn_fwd_fp16", "attn_debug_qk_int32",
     "attn_debug_qk_int32_fused_q",
     "attn_status_string", "attn_quantize_qk_fp8", "attn_fwd_fp8", "attn_v_fp8_stride",
@@ -68,6 +70,8 @@ def lib():
     L.attn_fwd_int8.restype = ctypes.c_int
     L.attn_quantize_k.argtypes = [SP, P, P, P, P, P, P]
     L.attn_quantize_k.restype = ctypes.c_int
+    L.attn_quantize_k_noalloc.argtypes = [SP, P, P, P, P, P]
+    L.attn_quantize_k_noalloc.restype = ctypes.c_int
     L.attn_fwd_int8_fused_q.argtypes = [SP, P, P, P, P, P, P, P, P, ctypes.c_int, F32, P]
     L.attn_fwd_int8_fused_q.restype = ctypes.c_int
     L.attn_fwd_fp16.argtypes = [SP, P, P, P, P, P, P, ctypes.c_int, F32, P]

@@ -227,6 +227,24 @@ int attn_quantize_k(const attn_shape* shape, const void* k_f16, int8_t* k_i8, fl
                            static_cast<hipStream_t>(stream));
 }
 
+int attn_quantize_k_noalloc(const attn_shape* shape, const void* k_f16, int8_t* k_i8, float* k_scale,
+                            float* k_mean, void* stream) {
+    int st = check_shape(shape);
+    if (st != ATTN_OK) return st;
+    if (!k_f16 || !k_i8 || !k_scale) return ATTN_EINVAL;
+    if (!aligned(k_f16, 16) || !aligned(k_i8, 16) || !aligned(k_scale, 4) || (k_mean && !aligned(k_mean, 4)))
+        return ATTN_EINVAL;
+    size_t mean_off = 0;
+    QuantWorkspace ws;
+    if (quant_workspace_layout(*shape, &mean_off, &ws.nchunk) > ATTN_NOALLOC_SCRATCH_BYTES) return ATTN_ESCRATCH;
+    void* scratch = nullptr;
+    if ((st = noalloc_scratch(&scratch)) != ATTN_OK) return st;
+    ws.partial = static_cast<long long*>(scratch);
+    ws.mean = reinterpret_cast<float*>(static_cast<char*>(scratch) + mean_off);
+    return launch_quantize(*shape, nullptr, k_f16, nullptr, nullptr, k_i8, k_scale, k_mean, ws,
+                           static_cast<hipStream_t>(stream));
+}
+
 int attn_fwd_int8_fused_q(const attn_shape* shape, const void* q_f16, const int8_t* k_i8,
                           const float* k_scale, const void* v_f16, void* o_f16, float* lse,
                           float* q_scale_out, const int32_t* kv_head_map, int causal,
@@ -565,6 +583,7 @@ const char* attn_status_string(int status) {
         case ATTN_EUNSUPPORTED: return "unsupported shape";
         case ATTN_ELAUNCH: return "kernel launch failed";
         case ATTN_ERANGE: return "kv_head_map entry out of range";
+        case ATTN_ESCRATCH: return "shape exceeds the no-allocation scratch buffer (ATTN_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }

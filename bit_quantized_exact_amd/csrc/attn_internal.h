@@ -36,6 +36,11 @@ struct QuantWorkspace {
 // Offsets of the workspace pieces for a shape (256-byte aligned pieces).
 size_t quant_workspace_layout(const attn_shape& s, size_t* mean_offset, int* nchunk);
 
+// The device address of the library's no-allocation scratch (ATTN_NOALLOC_
+// SCRATCH_BYTES, one copy per device) on the current device, looked up once
+// per device; ATTN_ELAUNCH when the lookup fails.
+int noalloc_scratch(void** ptr);
+
 // q may be null (K only): then q_i8 and q_scale are not touched.  fp8
 // selects E4M3 codes (stored in the int8 buffers) instead of INT8.
 int launch_quantize(const attn_shape& s, const void* q, const void* k, int8_t* q_i8,

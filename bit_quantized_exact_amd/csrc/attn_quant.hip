@@ -26,6 +26,7 @@
 #include "attn_internal.h"
 
 #include <cfloat>
+#include <mutex>
 
 namespace attn {
 namespace {
@@ -427,6 +428,27 @@ int launch_quantize_d(const attn_shape& s, const void* q, const void* k, int8_t*
 }
 
 }  // namespace
+
+// The workspace of attn_quantize_k_noalloc: a file-scope device array.  In
+// host code its name is only a stand-in for the symbol; the device address is
+// looked up per device with hipGetSymbolAddress (each device holds its own
+// copy at its own address) and only that address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
+int noalloc_scratch(void** ptr) {
+    static std::mutex mu;
+    static void* addr[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return ATTN_ELAUNCH;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return ATTN_ELAUNCH;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return ATTN_OK;
+}
 
 size_t quant_workspace_layout(const attn_shape& s, size_t* mean_offset, int* nchunk) {
     const int nc = ceil_div(s.seq, kSumChunk);

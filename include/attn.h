@@ -28,9 +28,10 @@
  *   one sequence length.  head_dim must be 64 or 128.
  * Memory.  Every tensor pointer is DEVICE memory owned by the caller, 16-byte
  *   aligned.  The library allocates and frees nothing and keeps no mutable
- *   global state beyond a per-device cache of the compute-unit count (which
- *   sizes the forward launches); calls are thread-safe.  kv_head_map is a
- *   HOST pointer.
+ *   global state beyond per-device caches of the compute-unit count (which
+ *   sizes the forward launches) and of the address of its no-allocation
+ *   scratch array (attn_quantize_k_noalloc); calls are thread-safe.
+ *   kv_head_map is a HOST pointer.
  * Execution.  Every call enqueues its kernels on `stream` (a hipStream_t; NULL
  *   means the null stream) and returns without synchronising.
  * Errors.  Calls return a status code and never throw.  All argument checks run
@@ -68,7 +69,8 @@ enum {
     ATTN_EINVAL = -1,       /* null pointer, non-positive size, misalignment, bad argument */
     ATTN_EUNSUPPORTED = -2, /* head_dim not 64/128, too many heads, sequence too long */
     ATTN_ELAUNCH = -3,      /* a kernel launch failed */
-    ATTN_ERANGE = -4        /* kv_head_map entry outside [0, heads_kv) */
+    ATTN_ERANGE = -4,       /* kv_head_map entry outside [0, heads_kv) */
+    ATTN_ESCRATCH = -5      /* the shape needs more than the no-allocation scratch holds */
 };
 
 #define ATTN_MAX_HEADS 256
@@ -133,6 +135,24 @@ int attn_fwd_int8(const attn_shape* shape, const int8_t* q_i8, const float* q_sc
  * with attn_fwd_int8_fused_q. */
 int attn_quantize_k(const attn_shape* shape, const void* k_f16, int8_t* k_i8, float* k_scale,
                     float* k_mean, void* workspace, void* stream);
+
+/* attn_quantize_k for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels, outputs and bit-exact results, with the workspace taken
+ * from a scratch array of ATTN_NOALLOC_SCRATCH_BYTES that the library keeps
+ * in device memory (one per GPU it runs on, held until the process ends)
+ * instead of a caller buffer.  The call allocates nothing (no hipMalloc, no
+ * allocating library routine); the caller still passes K and the outputs.
+ * Shapes whose attn_quantize_workspace_bytes exceed the scratch are rejected
+ * with ATTN_ESCRATCH before anything is launched (the scratch holds, e.g., 32
+ * (batch, kv-head) pairs of 65536 tokens at head_dim 128).  The scratch needs
+ * no initial contents (every byte is written before it is read), but it is
+ * shared by every call on one GPU: calls that overlap on one GPU (other
+ * streams, other host threads) race and must be ordered by the caller.
+ * ATTN_ELAUNCH also reports a failed lookup of the scratch's device address. */
+#define ATTN_NOALLOC_SCRATCH_BYTES (16u << 20)
+int attn_quantize_k_noalloc(const attn_shape* shape, const void* k_f16, int8_t* k_i8, float* k_scale,
+                            float* k_mean, void* stream);
 
 /* 8-bit attention forward that quantises Q itself: Q is read as fp16 and
  * each BQ-row block is quantised inside the forward kernel with exactly the

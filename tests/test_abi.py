@@ -42,7 +42,7 @@ def test_quant_blocks_and_status_strings():
     assert A.quant_blocks() == (128, 64)
     L = A.lib()
     assert L.attn_quant_blocks(None, None) == 0
-    for st in (0, -1, -2, -3, -4):
+    for st in (0, -1, -2, -3, -4, -5):
         assert A.status_string(st) and A.status_string(st) != "unknown status"
     assert A.status_string(7) == "unknown status"
 
@@ -178,6 +178,30 @@ def test_debug_null_and_alignment():
     bad = (ctypes.c_int32 * 4)(0, 1, 2, 0)
     assert F(ctypes.byref(sh), FAKE, FAKE, ctypes.cast(bad, ctypes.c_void_p), 0, 0, 0, FAKE, None, None) == -4
     assert F(ctypes.byref(_sh(D=96)), FAKE, FAKE, None, 0, 0, 0, FAKE, None, None) == -2
+
+
+def test_quantize_k_noalloc_rejects_on_the_host():
+    """Argument checks and the scratch limit run before any HIP call."""
+    L = A.lib()
+    F = L.attn_quantize_k_noalloc
+    sh = _sh(Hq=2, Hkv=2)
+    assert F(None, FAKE, FAKE, FAKE, None, None) == -1
+    assert F(ctypes.byref(sh), None, FAKE, FAKE, None, None) == -1
+    assert F(ctypes.byref(sh), FAKE, None, FAKE, None, None) == -1
+    assert F(ctypes.byref(sh), FAKE, FAKE, None, None, None) == -1
+    assert F(ctypes.byref(sh), MISALIGNED, FAKE, FAKE, None, None) == -1
+    assert F(ctypes.byref(sh), FAKE, MISALIGNED, FAKE, None, None) == -1
+    assert F(ctypes.byref(sh), FAKE, FAKE, FAKE + 2, None, None) == -1
+    assert F(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE + 2, None) == -1
+    assert F(ctypes.byref(_sh(D=96)), FAKE, FAKE, FAKE, None, None) == -2
+    # the largest shapes that fit, and the smallest that do not
+    cap = _native.ATTN_NOALLOC_SCRATCH_BYTES
+    fits = A.AttnShape(32, 1, 1, 65536, 128)
+    assert 0 < A.quantize_workspace_bytes(fits) <= cap
+    too_big = A.AttnShape(64, 1, 1, 65536, 128)
+    assert A.quantize_workspace_bytes(too_big) > cap
+    assert F(ctypes.byref(too_big), FAKE, FAKE, FAKE, None, None) == -5
+    assert "scratch" in A.status_string(-5)
 
 
 # --------------------------------------------------------------------------
