@@ -48,9 +48,20 @@ int build_map(const attn_shape& s, const int32_t* user_map, FwdParams* p) {
         }
     }
     int n = 0;
-    for (int k = 0; k < s.heads_kv; ++k)
+    bool uniform = s.heads_q % s.heads_kv == 0;
+    for (int k = 0; k < s.heads_kv; ++k) {
+        const int n0 = n;
         for (int h = 0; h < s.heads_q; ++h)
             if (p->kvmap[h] == k) p->horder[n++] = static_cast<uint8_t>(h);
+        if (n - n0 != s.heads_q / s.heads_kv) uniform = false;
+    }
+    // Launch-order groups (the q-heads of one kv-head, when all are the same
+    // size): only when one kv-head's K and V exceed the 4 MB L2 of an XCD.
+    // Smaller ones stay L2-resident in any order, and there the per-head order
+    // pairs heavy and light causal tiles better (measured: the 1024-token
+    // batched MQA workload runs 4 % slower grouped).
+    const bool big_kv = 4.0 * s.seq * s.head_dim > 4.0 * 1024 * 1024;
+    p->group = uniform && big_kv ? s.heads_q / s.heads_kv : 1;
     return ATTN_OK;
 }
 

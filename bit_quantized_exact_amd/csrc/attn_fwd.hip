@@ -383,7 +383,7 @@ void fwd_kernel(const FwdParams p_in) {
     float scale_log2 = p.scale_log2;
     if constexpr (PERSIST) asm volatile("" : "+s"(scale_log2));
     // (tile masks are mostly causal-like too, heavier for later query tiles)
-    const geom::BlockCoord bc = geom::decode_item(item, p.Hq, p.ntiles, p.tile_lo, CAUSAL || BMASK);
+    const geom::BlockCoord bc = geom::decode_item(item, p.Hq, p.ntiles, p.tile_lo, CAUSAL || BMASK, p.group);
     const int b = bc.b;
     const int h = p.horder[bc.pos];
     const int kvh = p.kvmap[h];
@@ -582,10 +582,23 @@ void fwd_kernel(const FwdParams p_in) {
                 asm volatile("" : "+v"(kaddr[st][s]));
             }
     }
-    // K scale of key tile t (clamped to the last block; tiles past the end are never used)
+    // K scale of key tile t (clamped to the last block; tiles past the end are
+    // never used).  The base and the block count are read once per item into
+    // registers: read through p per tile, they are reloaded after every copy
+    // block (whose memory clobber invalidates them), with a scalar load whose
+    // wait also drains the LDS reads.
+    // (a global-address-space pointer: as a generic one it would be read with
+    // a flat load, which also counts against the LDS reads' wait counter)
+    typedef const __attribute__((address_space(1))) float gfloat;
+    gfloat* ks_base = (gfloat*)(p.k_scale + (INT8 && !DUMP ? bhk * p.nkblk : 0));
+    int ks_last = p.nkblk - 1;
+    if constexpr (PERSIST) {
+        asm volatile("" : "+s"(ks_base));
+        asm volatile("" : "+s"(ks_last));
+    }
     auto kscale_at = [&](int t) -> float {
         if constexpr (BMASK) t = tile_row(t) / kBN;   // (list position -> key tile)
-        return p.k_scale[bhk * p.nkblk + geom::imin(t, p.nkblk - 1)];
+        return ks_base[geom::imin(t, ks_last)];
     };
     float ksring[3] = {1.0f, 1.0f, 1.0f};
 

@@ -28,9 +28,10 @@ constexpr int kSumChunk = 256;
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 struct QuantWorkspace {
-    long long* partial;   // [B*Hkv, nchunk, D] exact channel sums, units of 2^-24
-    float* mean;          // [B*Hkv, D]
-    int nchunk;
+    long long* partial;   // [B*Hkv, <= nchunk, D] exact channel sums, units of 2^-24 (K);
+                          // [B*Hkv, nchunk, D] channel maxima as fp32 (the 8-bit V)
+    float* mean;          // [B*Hkv, D] (part of the workspace size; no kernel needs it)
+    int nchunk;           // chunks of kSumChunk tokens
 };
 
 // Offsets of the workspace pieces for a shape (256-byte aligned pieces).
@@ -71,6 +72,7 @@ struct FwdParams {
     int nqblk, nkblk;     // scale blocks per (b, head)
     int tile_lo, ntiles;  // query tiles handled by this launch
     float scale_log2;     // sm_scale * log2(e)
+    int group;            // q-heads per kv-head when every kv-head has the same number, else 1
     uint8_t kvmap[ATTN_MAX_HEADS];   // q-head -> kv-head
     uint8_t horder[ATTN_MAX_HEADS];  // q-heads ordered by kv-head (launch order)
 };

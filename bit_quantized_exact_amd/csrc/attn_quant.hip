@@ -20,11 +20,12 @@
 //     compiled with -ffp-contract=off so that no product is fused.
 //
 // The kernels stream HBM: each reads its inputs once (K twice: sums, then
-// quantisation) with 16-byte loads and writes int8 with 8-byte stores.  Up to
-// 8192 tokens the K quantiser adds the chunk sums of its (b, kv-head) itself,
-// so K takes two launches (sums, quantisation) instead of three.
+// quantisation) with 16-byte loads and writes int8 with 8-byte stores.  The K
+// quantiser adds the (at most 32) partial sums of its (b, kv-head) itself, so
+// K takes two launches (sums, quantisation) at any length.
 #include "attn_internal.h"
 
+#include <algorithm>
 #include <cfloat>
 #include <mutex>
 
@@ -41,91 +42,79 @@ __device__ __forceinline__ float half_bits_to_float(unsigned h) {
     return static_cast<float>(x);
 }
 
-// Per (b, kv-head, chunk of kSumChunk tokens): exact column sums of K.
-// Thread t owns one 16-byte column chunk (8 channels) and every RG-th row of
-// the chunk; all of its row loads are issued before the first add (rows past
-// the sequence read the last row and are dropped).  The sums are taken in
-// fp64, which is exact here: every fp16 value is an integer multiple of 2^-24
-// below 2^40 in those units, so any sum of at most kSumChunk of them is such
-// a multiple below 2^48 < 2^53.  The chunk total is then stored as that
-// integer (int64), which keeps the cross-chunk total exact in any order.
+// Per (b, kv-head, group of cps chunks of kSumChunk tokens): exact column
+// sums of K.  Thread t owns one 16-byte column chunk (8 channels) and every
+// RG-th row of each chunk; per chunk all of its row loads are issued before
+// the first add (rows past the sequence read the last row and are dropped).
+// Each thread sums in fp64, which is exact here: every fp16 value is an
+// integer multiple of 2^-24 below 2^40 in those units, and a thread adds at
+// most cps * kSumChunk / RG <= 4096 of them (cps <= 512 for S <= 2^22), so
+// its sum is such a multiple below 2^52 < 2^53.  It is converted to that
+// integer (int64) before the threads of a column are added, so the group
+// total (below 2^57) and any later total are exact in any order.  Grouping
+// chunks keeps the partials per (b, kv-head) at kMaxPartials, few enough for
+// the K quantiser to add them itself (no mean launch).
 constexpr int kColsumThreads = 512;
+constexpr int kMaxPartials = 32;
 template <int D>
 __global__ __launch_bounds__(kColsumThreads) void k_colsum_kernel(const uint16_t* __restrict__ k, int S,
-                                                                  int nchunk,
+                                                                  int cps, int npart,
                                                                   long long* __restrict__ partial) {
     constexpr int CPR = D / 8;                  // 16-byte chunks per row
     constexpr int RG = kColsumThreads / CPR;    // row groups
-    constexpr int RPT = kSumChunk / RG;         // rows per thread
-    static_assert(kSumChunk % RG == 0 && kSumChunk * 65536.0 * 16777216.0 < 9007199254740992.0,
-                  "exact fp64 chunk sums");
-    __shared__ double red[RG][D];
+    constexpr int RPT = kSumChunk / RG;         // rows per thread per chunk
+    static_assert(kSumChunk % RG == 0 && 512 * RPT <= 4096 && 4096.0 * 65536.0 * 16777216.0 < 9007199254740992.0,
+                  "exact fp64 thread sums");
+    __shared__ long long red[RG][D];
     const int t = threadIdx.x;
     const int cc = t % CPR, rg = t / CPR;
-    const int chunk = blockIdx.x;
+    const int grp = blockIdx.x;
     const size_t bk = blockIdx.y;
     const uint16_t* base = k + bk * static_cast<size_t>(S) * D + cc * 8;
-    const int r0 = chunk * kSumChunk + rg;
-    i4x v[RPT];
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const int r = r0 + i * RG;
-        v[i] = *reinterpret_cast<const i4x*>(base + static_cast<size_t>(r < S ? r : S - 1) * D);
-    }
     double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    // the rows of chunk c of the group (rows past the sequence read the last row)
+    auto load = [&](int c, i4x (&v)[RPT]) __attribute__((always_inline)) {
+        const int r0 = (grp * cps + c) * kSumChunk + rg;
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        if (r0 + i * RG >= S) break;
+        for (int i = 0; i < RPT; ++i) {
+            const int r = r0 + i * RG;
+            v[i] = *reinterpret_cast<const i4x*>(base + static_cast<size_t>(r < S ? r : S - 1) * D);
+        }
+    };
+    auto add = [&](int c, const i4x (&v)[RPT]) __attribute__((always_inline)) {
+        const int r0 = (grp * cps + c) * kSumChunk + rg;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const unsigned w = static_cast<unsigned>(v[i][e]);
-            acc[2 * e] += static_cast<double>(half_bits_to_float(w & 0xffffu));
-            acc[2 * e + 1] += static_cast<double>(half_bits_to_float(w >> 16));
+        for (int i = 0; i < RPT; ++i) {
+            if (r0 + i * RG >= S) break;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const unsigned w = static_cast<unsigned>(v[i][e]);
+                acc[2 * e] += static_cast<double>(half_bits_to_float(w & 0xffffu));
+                acc[2 * e + 1] += static_cast<double>(half_bits_to_float(w >> 16));
+            }
+        }
+    };
+    // the chunks of the group (those starting inside the sequence), with the
+    // next chunk's loads in flight while the current one is added
+    const int nc = min(cps, (S + kSumChunk - 1) / kSumChunk - grp * cps);
+    i4x va[RPT], vb[RPT];
+    if (nc > 0) load(0, va);
+    for (int c = 0; c < nc; c += 2) {
+        if (c + 1 < nc) load(c + 1, vb);
+        add(c, va);
+        if (c + 1 < nc) {
+            if (c + 2 < nc) load(c + 2, va);
+            add(c + 1, vb);
         }
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) red[rg][cc * 8 + e] = acc[e];
+    for (int e = 0; e < 8; ++e) red[rg][cc * 8 + e] = static_cast<long long>(__builtin_ldexp(acc[e], 24));
     __syncthreads();
     if (t < D) {
-        double s = 0.0;
+        long long s = 0;
 #pragma unroll
         for (int g = 0; g < RG; ++g) s += red[g][t];
-        partial[(bk * nchunk + chunk) * D + t] = static_cast<long long>(__builtin_ldexp(s, 24));
-    }
-}
-
-// Per (b, kv-head): total over chunks, mu = fp32(fp64(sum) / S).  kMeanGroups
-// threads per channel each add every kMeanGroups-th chunk (loads unrolled so
-// they are in flight together), then LDS combines the groups.
-constexpr int kMeanGroups = 4;
-template <int D>
-__global__ __launch_bounds__(D * kMeanGroups) void k_mean_kernel(const long long* __restrict__ partial, int S,
-                                                                 int nchunk, float* __restrict__ mean,
-                                                                 float* __restrict__ mean_out) {
-    __shared__ long long red[kMeanGroups][D];
-    const size_t bk = blockIdx.x;
-    const int c = threadIdx.x % D, grp = threadIdx.x / D;
-    const long long* src = partial + bk * static_cast<size_t>(nchunk) * D + c;
-    long long s[4] = {0, 0, 0, 0};
-    int i = grp;
-    for (; i + 3 * kMeanGroups < nchunk; i += 4 * kMeanGroups) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) s[u] += src[static_cast<size_t>(i + u * kMeanGroups) * D];
-    }
-    for (; i < nchunk; i += kMeanGroups) s[0] += src[static_cast<size_t>(i) * D];
-    red[grp][c] = (s[0] + s[1]) + (s[2] + s[3]);
-    __syncthreads();
-    if (grp == 0) {
-        long long tot = 0;
-#pragma unroll
-        for (int g = 0; g < kMeanGroups; ++g) tot += red[g][c];
-        // (double)tot is exact below 2^53 and correctly rounded above; the
-        // 2^-24 scaling is exact; the division and the narrowing are IEEE
-        // operations.
-        const double total = __builtin_ldexp(static_cast<double>(tot), -24);
-        const float mu = static_cast<float>(total / static_cast<double>(S));
-        mean[bk * D + c] = mu;
-        if (mean_out) mean_out[bk * D + c] = mu;
+        partial[(bk * npart + grp) * D + t] = s;
     }
 }
 
@@ -138,10 +127,14 @@ __device__ __forceinline__ float block_max(float v, float* red) {
     return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
-__device__ __forceinline__ int quant_one(float x, float r) {
-    float t = __builtin_rintf(x * r);
-    t = fminf(fmaxf(t, -127.0f), 127.0f);
-    return static_cast<int>(t);
+// INT8 code of x with r = 127 / a, |x| <= a: clamp(rint(x r), -127, 127) as
+// the low byte of fp32(fp32(x r) + 1.5 * 2^23).  |x r| <= 127 (1 + 2^-24)^2
+// < 127.5, so the clamp never acts, and adding 1.5 * 2^23 rounds x r to an
+// integer (to nearest, ties to even, as rint) held in the low mantissa bits.
+// (The product and the sum are rounded separately: this file is compiled
+// without contraction.)
+__device__ __forceinline__ unsigned quant_byte(float x, float r) {
+    return __float_as_uint(x * r + 12582912.0f) & 0xffu;
 }
 
 // E4M3 codes of x0*r, x1*r (saturated to +-448 first) in bytes 0 and 1 of
@@ -156,11 +149,13 @@ __device__ __forceinline__ unsigned e4m3_pair(float x0, float x1, float r) {
 // SMOOTH subtracts the channel mean first (K); Q is quantised as is.  FP8
 // selects the E4M3 grid (448 in place of 127, E4M3 rounding in place of
 // rint + clamp): the FP8 alternative the SageAttention article compares with.
-// MEANP (with SMOOTH): the workgroup adds the per-chunk exact channel sums of
-// its (b, kv-head) itself - the same integer totals and the same division as
-// k_mean_kernel, so the same means - instead of reading them from `mean`;
-// for short sequences this saves the separate mean launch.  The block with
-// blk == 0 writes the means to mean_out when it is not null.
+// MEANP (with SMOOTH, the form the K path uses): the workgroup adds the
+// exact partial channel sums of its (b, kv-head) itself (at most
+// kMaxPartials int64 values per channel) and divides once, mu =
+// fp32(fp64(sum) / S), instead of reading means from `mean`; every
+// workgroup of a (b, kv-head) forms the same integer total, so the same
+// means.  The block with blk == 0 writes the means to mean_out when it is
+// not null.
 template <int D, int ROWS, bool SMOOTH, bool FP8 = false, bool MEANP = false>
 __global__ __launch_bounds__(256) void quant_block_kernel(const uint16_t* __restrict__ x,
                                                           const float* __restrict__ mean,
@@ -168,20 +163,19 @@ __global__ __launch_bounds__(256) void quant_block_kernel(const uint16_t* __rest
                                                           float* __restrict__ scale, int H,
                                                           int S, int nblk,
                                                           const long long* __restrict__ partial,
-                                                          int nchunk, float* __restrict__ mean_out) {
+                                                          int nchunk, float* __restrict__ mean_out,
+                                                          int bpw) {
     constexpr float kTop = FP8 ? 448.0f : 127.0f;
     constexpr int CPR = D / 8;
     constexpr int CHUNKS = ROWS * CPR;
     constexpr int PER = CHUNKS / 256;
     static_assert(CHUNKS % 256 == 0, "chunks must split evenly");
-    __shared__ float red[4];
+    __shared__ float red[2][4];
     const int t = threadIdx.x;
     const int cc = t % CPR;   // 256 % CPR == 0: the column chunk is fixed per thread
-    const int blk = blockIdx.x;
     const size_t mat = static_cast<size_t>(blockIdx.z) * H + blockIdx.y;
     const uint16_t* xb = x + mat * static_cast<size_t>(S) * D;
     int8_t* qb = q + mat * static_cast<size_t>(S) * D;
-    const int r0 = blk * ROWS;
 
     float mu[8];
     if constexpr (MEANP) {
@@ -207,7 +201,7 @@ __global__ __launch_bounds__(256) void quant_block_kernel(const uint16_t* __rest
             const double total = __builtin_ldexp(static_cast<double>(tot), -24);
             const float m = static_cast<float>(total / static_cast<double>(S));
             smu[c] = m;
-            if (mean_out && blk == 0) mean_out[mat * D + c] = m;
+            if (mean_out && blockIdx.x == 0) mean_out[mat * D + c] = m;
         }
         __syncthreads();
 #pragma unroll
@@ -217,6 +211,12 @@ __global__ __launch_bounds__(256) void quant_block_kernel(const uint16_t* __rest
         for (int e = 0; e < 8; ++e) mu[e] = SMOOTH ? mean[mat * D + cc * 8 + e] : 0.0f;
     }
 
+    // bpw consecutive blocks per workgroup (the means above are formed once
+    // for all of them); the block maxima alternate between two LDS slots
+    for (int bi = 0; bi < bpw; ++bi) {
+    const int blk = blockIdx.x * bpw + bi;
+    if (blk >= nblk) break;   // (workgroup-uniform)
+    const int r0 = blk * ROWS;
     float v[PER][8];
     float amax = 0.0f;
 #pragma unroll
@@ -243,7 +243,7 @@ __global__ __launch_bounds__(256) void quant_block_kernel(const uint16_t* __rest
 #pragma unroll
         for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[i][e]));
     }
-    const float a = block_max(amax, red);
+    const float a = block_max(amax, red[bi & 1]);
     const float r = (a == 0.0f) ? 0.0f : __fdiv_rn(kTop, a);
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(256) void quant_block_kernel(const uint16_t* __rest
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const unsigned b8 = static_cast<unsigned>(quant_one(v[i][e], r)) & 0xffu;
+                    const unsigned b8 = quant_byte(v[i][e], r);
                     packed[e / 4] |= b8 << (8 * (e % 4));
                 }
             }
@@ -267,6 +267,7 @@ __global__ __launch_bounds__(256) void quant_block_kernel(const uint16_t* __rest
         }
     }
     if (t == 0) scale[mat * nblk + blk] = (a == 0.0f) ? 0.0f : __fdiv_rn(a, kTop);
+    }
 }
 
 // 8-bit V of the P.V ablation, pass 1: per (b, kv-head, chunk of kSumChunk
@@ -392,11 +393,6 @@ __global__ __launch_bounds__(256) void v_quant_kernel(const uint16_t* __restrict
     }
 }
 
-// Up to this many chunk sums per (b, kv-head) (sequences up to 8192 tokens)
-// the K quantiser adds them itself; longer sequences keep the mean kernel,
-// whose one reduction per (b, kv-head) is cheaper than one per K block.
-constexpr int kMeanInQuantMaxChunks = 32;
-
 template <int D, bool FP8>
 int launch_quantize_d(const attn_shape& s, const void* q, const void* k, int8_t* q_i8,
                       float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
@@ -405,25 +401,25 @@ int launch_quantize_d(const attn_shape& s, const void* q, const void* k, int8_t*
     const int BH_kv = s.batch * s.heads_kv;
     const uint16_t* kk = static_cast<const uint16_t*>(k);
     const uint16_t* qq = static_cast<const uint16_t*>(q);
-    hipLaunchKernelGGL(k_colsum_kernel<D>, dim3(ws.nchunk, BH_kv), dim3(kColsumThreads), 0, st, kk, S,
-                       ws.nchunk, ws.partial);
+    // chunks per column-sum workgroup, so that at most kMaxPartials partial
+    // sums per (b, kv-head) remain for the K quantiser to add
+    const int cps = ceil_div(ws.nchunk, kMaxPartials);
+    const int npart = ceil_div(ws.nchunk, cps);
+    hipLaunchKernelGGL(k_colsum_kernel<D>, dim3(npart, BH_kv), dim3(kColsumThreads), 0, st, kk, S, cps, npart,
+                       ws.partial);
     const int nkb = ceil_div(S, kBK), nqb = ceil_div(S, kBQ);
-    if (ws.nchunk <= kMeanInQuantMaxChunks) {
-        hipLaunchKernelGGL((quant_block_kernel<D, kBK, true, FP8, true>), dim3(nkb, s.heads_kv, s.batch),
-                           dim3(256), 0, st, kk, static_cast<const float*>(nullptr), k_i8, k_scale, s.heads_kv,
-                           S, nkb, ws.partial, ws.nchunk, k_mean);
-    } else {
-        hipLaunchKernelGGL(k_mean_kernel<D>, dim3(BH_kv), dim3(D * kMeanGroups), 0, st, ws.partial, S, ws.nchunk,
-                           ws.mean, k_mean);
-        hipLaunchKernelGGL((quant_block_kernel<D, kBK, true, FP8>), dim3(nkb, s.heads_kv, s.batch),
-                           dim3(256), 0, st, kk, ws.mean, k_i8, k_scale, s.heads_kv, S, nkb,
-                           static_cast<const long long*>(nullptr), 0, static_cast<float*>(nullptr));
-    }
+    // K blocks per quantiser workgroup: one while that leaves at most 1024
+    // workgroups, else up to 8 (each workgroup adds the partial sums once
+    // for all of its blocks)
+    const int bpw = std::min(8, std::max(1, nkb * BH_kv / 1024));
+    hipLaunchKernelGGL((quant_block_kernel<D, kBK, true, FP8, true>), dim3(ceil_div(nkb, bpw), s.heads_kv, s.batch),
+                       dim3(256), 0, st, kk, static_cast<const float*>(nullptr), k_i8, k_scale, s.heads_kv,
+                       S, nkb, ws.partial, npart, k_mean, bpw);
     if (qq)
         hipLaunchKernelGGL((quant_block_kernel<D, kBQ, false, FP8>), dim3(nqb, s.heads_q, s.batch),
                            dim3(256), 0, st, qq, static_cast<const float*>(nullptr), q_i8, q_scale,
                            s.heads_q, S, nqb, static_cast<const long long*>(nullptr), 0,
-                           static_cast<float*>(nullptr));
+                           static_cast<float*>(nullptr), 1);
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ELAUNCH;
 }
 

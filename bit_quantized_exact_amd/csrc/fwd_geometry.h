@@ -25,15 +25,25 @@ struct BlockCoord {
     int qt;   // query tile
 };
 
-// Logical work item -> (batch, head position, query tile).  Causal launches
-// take the heaviest query tiles of a head first.  Bijective on [0, nitems).
-__host__ __device__ inline BlockCoord decode_item(int L, int Hq, int ntiles, int tile_lo, bool heavy_first) {
+// Logical work item -> (batch, head position, query tile).  Within a batch
+// the head positions (q-heads ordered by kv-head) form groups of G
+// consecutive positions, the q-heads that share a kv-head (G = 1 when the
+// groups are irregular); items run group by group and, inside a group,
+// rank-major: the G heads of a group take the same query tile one after the
+// other, so their workgroups read the same K/V tiles close together in time
+// (and mostly from L2).  Causal launches take the heaviest query tiles of a
+// head first.  Bijective on [0, nitems) when Hq is a multiple of G.
+__host__ __device__ inline BlockCoord decode_item(int L, int Hq, int ntiles, int tile_lo, bool heavy_first,
+                                                  int G = 1) {
     const int per_b = Hq * ntiles;
     BlockCoord c;
     c.b = L / per_b;
     const int rb = L - c.b * per_b;
-    c.pos = rb / ntiles;
-    const int rank = rb - c.pos * ntiles;
+    const int per_g = G * ntiles;
+    const int gi = rb / per_g;
+    const int r2 = rb - gi * per_g;
+    const int rank = r2 / G;
+    c.pos = gi * G + (r2 - rank * G);
     c.qt = tile_lo + (heavy_first ? (ntiles - 1 - rank) : rank);
     return c;
 }

@@ -36,7 +36,7 @@ static long g_errors = 0;
 // [D, 64 * nkblk] per (b, kv-head) instead of row-major fp16 V.
 template <int D, bool INT8>
 static void check_shape(int B, int Hq, int S, bool causal, bool dump, int tile_lo, int ntiles,
-                        bool all_heads, bool pv8 = false) {
+                        bool all_heads, bool pv8 = false, int G = 1) {
     using St = Stage<D, INT8>;
     const int nqt = (S + kTileM - 1) / kTileM;
     if (!dump) {
@@ -73,7 +73,7 @@ static void check_shape(int B, int Hq, int S, bool causal, bool dump, int tile_l
     std::fill(seen.begin(), seen.end(), 0);
     for (const auto& w : work) {
         const int item = w.second;
-        const BlockCoord c = decode_item(item, Hq, ntiles, tile_lo, causal);
+        const BlockCoord c = decode_item(item, Hq, ntiles, tile_lo, causal, G);
         REQUIRE(c.b >= 0 && c.b < B && c.pos >= 0 && c.pos < Hq && c.qt >= tile_lo &&
                     c.qt < tile_lo + ntiles && c.qt < nqt,
                 "item %d -> b %d pos %d qt %d", item, c.b, c.pos, c.qt);
@@ -252,6 +252,12 @@ static void check_all_paths(int B, int Hq, int S, bool all_heads) {
     for (int causal = 0; causal < 2; ++causal) {
         check_shape<D, false>(B, Hq, S, causal, false, 0, 0, all_heads);
         check_shape<D, true>(B, Hq, S, causal, false, 0, 0, all_heads);
+        // launch-order groups of q-heads sharing a kv-head (every divisor of Hq)
+        for (int G = 2; G <= Hq; ++G)
+            if (Hq % G == 0) {
+                check_shape<D, false>(B, Hq, S, causal, false, 0, 0, all_heads, false, G);
+                check_shape<D, true>(B, Hq, S, causal, true, 0, nqt, all_heads, false, G);
+            }
         check_shape<D, true>(B, Hq, S, causal, false, 0, 0, all_heads, true);
         check_shape<D, true>(B, Hq, S, causal, true, 0, nqt, all_heads);
         check_shape<D, true>(B, Hq, S, causal, true, nqt - 1, 1, all_heads);

@@ -1,5 +1,6 @@
-"""Host check of the rounding identity the fused-Q forward kernel uses to
-form INT8 codes (no GPU).
+"""Host check of the rounding identity the INT8 quantisers use to form codes
+(no GPU): the fused-Q forward kernel on fp16 Q, and the standalone quantiser
+on fp16 Q and on the smoothed K (fp32 values x = fp32(k) - mu).
 
 The kernel quantises x (fp16) with r = fp32(127 / a), a = max|x| of the block,
 as the low byte of fp32(fp32(x * r) + 1.5 * 2^23) instead of
@@ -53,3 +54,20 @@ def test_bit_pattern_maximum_is_magnitude_maximum():
         h = rng.standard_normal(256).astype(np.float16) * np.float16(rng.uniform(0.01, 100))
         pat = (h.view(np.uint16) & 0x7FFF)
         assert np.uint16(pat.max()).view(np.float16) == np.abs(h).max()
+
+
+def test_identity_for_fp32_values():
+    """The standalone quantiser applies the same identity to the smoothed K,
+    whose values are fp32 numbers (fp32(k) - mu); checked on random fp32 x with
+    |x| <= a over a spread of block maxima, with the maximum itself, its
+    negative, exact half-way products and zero in every set."""
+    rng = np.random.default_rng(7)
+    for a in np.float32(2.0) ** rng.uniform(-20, 17, 300).astype(np.float32):
+        a = np.float32(a)
+        r = np.float32(np.float32(127.0) / a)
+        x = (rng.uniform(-1, 1, 4000) * a).astype(np.float32)
+        # products landing on n + 1/2 exactly (ties), where representable
+        halves = (np.arange(-127, 127) + np.float32(0.5)).astype(np.float32) / r
+        x = np.concatenate([x, [a, -a, np.float32(0)], halves[np.abs(halves) <= a].astype(np.float32)])
+        assert np.array_equal(_codes_kernel(x, r), _codes_rule(x, r)), a
+
