@@ -39,7 +39,7 @@ time (the clocks ramp up after the GPU idled while the CPU drew the inputs),
 then the W warm-up steps, then exactly K timed steps.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-       [--no-configs] [--no-cpu] [--clock-warm-ms MS]
+       [--no-configs] [--no-cpu] [--clock-warm-ms MS] [--only-step]
        python bench.py --decode-only [--decode-reps N]      (profiling)
        python bench.py --copy-calibration BYTES             (HBM counter scale)
 """
@@ -73,6 +73,9 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-workload block paths.configs")
+    ap.add_argument("--only-step", action="store_true",
+                    help="only the warm-up and timed steps of the workload (for profiling): no "
+                         "other paths, configs, decode, APB, MFMA loop or CPU baseline")
     ap.add_argument("--config-steps", type=int, default=10,
                     help="timed steps per workload in paths.configs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -619,6 +622,14 @@ def main():
         sys.exit(2)
     if args.decode_only:
         print(json.dumps(run_decode(reps=args.decode_reps)), flush=True)
+        return
+    if args.only_step:
+        from bit_quantized_exact_amd.inputs import WORKLOADS
+        w = WORKLOADS[args.workload]
+        t = time_core(w, args.steps, args.warmup)
+        print(json.dumps({"workload": args.workload, "steps": args.steps, "ms_quantize_k": round(t["ms_q"], 4),
+                          "ms_fwd_int8_fused_q": round(t["ms_8"], 4), "ms_fwd_fp16": round(t["ms_16"], 4)}),
+              flush=True)
         return
     rec = run_workload(args.workload, args.steps, args.warmup, cpu=not args.no_cpu,
                        cpu_seconds=args.cpu_seconds, configs=not args.no_configs,

@@ -682,7 +682,10 @@ void fwd_kernel(const FwdParams p_in) {
         // q = rint(x * r): |x * r| <= 127 (1 + 2^-23) here, so the clamp to
         // [-127, 127] never acts, and adding 1.5 * 2^23 rounds x * r to an
         // integer (nearest, ties to even, as rint) whose two's-complement low
-        // byte is the code.  (Product and sum rounded separately: no FMA.)
+        // byte is the code.  The product is rounded on its own, as
+        // fma(x, r, 0) (one rounding of the exact product, i.e. the fp32
+        // product, which lets the fp16 x feed a mixed-precision FMA
+        // directly), and the sum separately.
 #pragma unroll
         for (int s = 0; s < C::QSTEPS; ++s) {
             uint32_t w[4];
@@ -692,7 +695,7 @@ void fwd_kernel(const FwdParams p_in) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
 #pragma clang fp contract(off)
-                    const float t = static_cast<float>(qraw[s][e4 >> 1][(e4 & 1) * 4 + e]) * r;
+                    const float t = __builtin_fmaf(static_cast<float>(qraw[s][e4 >> 1][(e4 & 1) * 4 + e]), r, 0.0f);
                     b[e] = __float_as_uint(t + 12582912.0f);
                 }
                 const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);
