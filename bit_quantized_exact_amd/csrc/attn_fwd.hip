@@ -137,6 +137,10 @@ __device__ __forceinline__ float row_max(float x) {
     const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
     return a > b ? a : b;
 }
+__device__ __forceinline__ int row_max_i(int x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(x), static_cast<unsigned>(x), false, false);
+    return max(static_cast<int>(r[0]), static_cast<int>(r[1]));
+}
 __device__ __forceinline__ float row_sum(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
@@ -716,8 +720,10 @@ void fwd_kernel(const FwdParams p_in) {
         f16x oacc[C::DT];
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) oacc[dt] = f16x{};
-        float qscale = 1.0f;
-        if constexpr (INT8 && !DUMP) qscale = QF16 ? qscale_fused : p.q_scale[bhq * p.nqblk + qt];
+        // INT8: the per-tile score scale is (dQ sm_scale log2 e) dK_j
+        float qscale_log2 = scale_log2;
+        if constexpr (INT8 && !DUMP) qscale_log2 *= QF16 ? qscale_fused : p.q_scale[bhq * p.nqblk + qt];
+        float m_thr = -INFINITY;   // m_run plus the lazy headroom: a tile max above it raises m_run
         const float* kscale = p.k_scale;
 
         // ---- prologue: K_0 -> LDS, S_0, then K_1 and V_0 -> LDS (and, at
@@ -779,7 +785,7 @@ void fwd_kernel(const FwdParams p_in) {
             } else {
                 // scores in log2 units: s * c with c = (dQ dK) sm_scale log2(e)
                 float c = scale_log2;
-                if constexpr (INT8) c = fmaxf(qscale * kscale_j * scale_log2, FLT_MIN);
+                if constexpr (INT8) c = fmaxf(qscale_log2 * kscale_j, FLT_MIN);
                 float sv[2][16];
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt)
@@ -802,15 +808,26 @@ void fwd_kernel(const FwdParams p_in) {
                         for (int r = 0; r < 16; ++r)
                             if (!(key_offset(mt, r) < lim)) sv[mt][r] = -INFINITY;
                 }
-                float mx = sv[0][0];
+                float m_tile;
+                if constexpr (kBiased) {
+                    // biased scores are positive floats (masked ones -inf), so
+                    // they order as their bit patterns do as signed integers
+                    int mi = __float_as_int(sv[0][0]);
 #pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
+                    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, sv[mt][r]);
-                // (the biased maximum minus the bias is exact: both lie in [2^23, 2^24))
-                const float m_tile = (kBiased ? row_max(mx) - kI8Bias : row_max(mx)) * c;
-                // (8-bit P needs p <= 1: no lazy headroom there)
-                const bool raise = m_tile > m_run + (PV8 ? 0.0f : kLazy);
+                        for (int r = 0; r < 16; ++r) mi = max(mi, __float_as_int(sv[mt][r]));
+                    // (the biased maximum minus the bias is exact: both lie in [2^23, 2^24))
+                    m_tile = (__int_as_float(row_max_i(mi)) - kI8Bias) * c;
+                } else {
+                    float mx = sv[0][0];
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, sv[mt][r]);
+                    m_tile = row_max(mx) * c;
+                }
+                const bool raise = m_tile > m_thr;
                 if (__ballot(raise)) {
                     // (each row decides for itself: a row's result never depends on
                     // the scores of the other rows of the wave)
@@ -819,6 +836,8 @@ void fwd_kernel(const FwdParams p_in) {
                     // empty, alpha = 0 avoids exp2(-inf - -inf))
                     const float alpha = BMASK && m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
                     m_run = m_new;
+                    // (8-bit P needs p <= 1: no lazy headroom there)
+                    m_thr = m_new + (PV8 ? 0.0f : kLazy);
                     l_run *= alpha;
 #pragma unroll
                     for (int dt = 0; dt < C::DT; ++dt) oacc[dt] *= alpha;
