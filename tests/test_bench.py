@@ -1,5 +1,6 @@
 """Host-side checks of bench.py (no GPU): the one-GPU contract and the
 staleness rule of the committed HBM-counter summaries."""
+import glob
 import hashlib
 import os
 import subprocess
@@ -45,13 +46,15 @@ def test_counters_are_used_only_while_the_kernel_sources_match(tmp_path, monkeyp
 
 
 def test_committed_summaries_name_existing_sources():
-    for tag in ("fwd_fp16", "fwd_int8"):
-        path = os.path.join(ROOT, "profiles", f"{tag}_llm_prefill_gqa_counters.txt")
-        if not os.path.exists(path):
-            pytest.skip("no committed counter summary")
-        src = [l.split(":", 1)[1].split() for l in open(path) if l.startswith("source:")][0]
-        for name in src:
-            assert os.path.exists(os.path.join(ROOT, "bit_quantized_exact_amd", "csrc", name)), name
+    paths = sorted(glob.glob(os.path.join(ROOT, "profiles", "*_counters.txt")))
+    if not paths:
+        pytest.skip("no committed counter summary")
+    for path in paths:
+        vals = dict(l.split(":", 1) for l in open(path) if ":" in l and not l.startswith("#"))
+        for name in vals["source"].split():
+            assert os.path.exists(os.path.join(ROOT, "bit_quantized_exact_amd", "csrc", name)), (path, name)
+        for key in ("source_sha256", "hbm_bytes_per_launch", "algorithmic_bytes_per_launch"):
+            assert key in vals, (path, key)
 
 
 def test_peaks_are_the_published_dense_rates():
