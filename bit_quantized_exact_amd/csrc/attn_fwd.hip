@@ -589,12 +589,16 @@ void fwd_kernel(const FwdParams p_in) {
     // K scale of key tile t (clamped to the last block; tiles past the end are
     // never used).  The base and the block count are read once per item into
     // registers: read through p per tile, they are reloaded after every copy
-    // block (whose memory clobber invalidates them), with a scalar load whose
-    // wait also drains the LDS reads.
-    // (a global-address-space pointer: as a generic one it would be read with
-    // a flat load, which also counts against the LDS reads' wait counter)
-    typedef const __attribute__((address_space(1))) float gfloat;
-    gfloat* ks_base = (gfloat*)(p.k_scale + (INT8 && !DUMP ? bhk * p.nkblk : 0));
+    // block (whose memory clobber invalidates them).  The scales are read
+    // through a constant-address-space pointer at a wave-uniform index, i.e.
+    // with scalar loads: they count against neither the copies' wait counter
+    // (a vector load would, and the compiler's wait for it would drain the
+    // copies) nor, issued right before a stage barrier (which waits for the
+    // LDS and scalar counter anyway), the LDS reads' waits inside a tile.
+    // (The scales are written by the K quantiser before this kernel starts
+    // and are read-only while it runs.)
+    typedef const __attribute__((address_space(4))) float cfloat;
+    cfloat* ks_base = (cfloat*)(p.k_scale + (INT8 && !DUMP ? bhk * p.nkblk : 0));
     int ks_last = p.nkblk - 1;
     if constexpr (PERSIST) {
         asm volatile("" : "+s"(ks_base));
@@ -602,16 +606,40 @@ void fwd_kernel(const FwdParams p_in) {
     }
     auto kscale_at = [&](int t) -> float {
         if constexpr (BMASK) t = tile_row(t) / kBN;   // (list position -> key tile)
-        return ks_base[geom::imin(t, ks_last)];
+        return ks_base[__builtin_amdgcn_readfirstlane(geom::imin(t, ks_last))];
     };
     float ksring[3] = {1.0f, 1.0f, 1.0f};
 
     // The prologue's copies into LDS (K_0 .. K_{NST-1}, V_0 .. V_{NST-2})
-    // and Q's loads overlap.  The INT8 kernels issue the copies first (and
-    // the first K scales after them); the FP16 kernels load Q first, so that
-    // the first score tile waits for Q and K_0 only, not for the whole copy
-    // queue.  (Register staging: K_0's loads go out before Q.)
+    // and Q's loads overlap.  The FP16 kernels load Q first, so that the
+    // first score tile waits for Q and K_0 only, not for the whole copy queue;
+    // the INT8 kernel on INT8 Q issues the copies first.  The INT8 kernel
+    // that quantises fp16 Q itself copies Q into LDS first, into the stages
+    // of V_1 and V_2 (free until V_1's copies, which go out once every wave
+    // has read its Q rows), then K_0, K_1, V_0 and K_2: it waits for Q's
+    // copies alone (an explicit count of the copies after them), quantises Q
+    // while the tiles land, and only then issues V_1.  (Loaded into
+    // registers, Q would be waited for by the compiler, whose wait also
+    // covers every copy issued after the loads.)  (Register staging: K_0's
+    // loads go out before Q.)
     constexpr bool QFIRST = DTL && !INT8;
+    constexpr bool QLDS = DTL && QF16;
+    static_assert(!QLDS || NST == 3, "Q staging uses the stages of V_1 and V_2");
+    // copies of the query block's fp16 rows q0 + 64 h .. q0 + 64 h + 63 (rows
+    // past the sequence read row S-1) into a V-sized stage, 16-byte chunks
+    // XOR-swizzled by row as in the K stages (row-wise reads below)
+    auto dtl_q = [&](int h, char* st) __attribute__((always_inline)) {
+        const int first = geom::tile_first_row(q0 + kBN * h, S);
+        const char* base = static_cast<const char*>(p.q) + (bhq * S + static_cast<size_t>(first)) * C::VROWG;
+        uint32_t off[DV::NI];
+#pragma unroll
+        for (int i = 0; i < DV::NI; ++i) {
+            const int r = DV::slot_row(wave, i, lane);
+            const int c = DV::slot_chunk(wave, i, lane) ^ DV::k_swz(r);
+            off[i] = static_cast<uint32_t>(geom::tile_lane_row(r, first, S)) * C::VROWG + c * 16;
+        }
+        dtl_copies<DV::NI>(base, off, st + wave_s * DV::NI * 1024);
+    };
     auto dtl_prologue = [&]() __attribute__((always_inline)) {
         dtl_k(tile_row(0), dks[0]);
         dtl_k(tile_row(1), dks[1]);
@@ -622,7 +650,16 @@ void fwd_kernel(const FwdParams p_in) {
         }
     };
     if constexpr (DTL && !QFIRST) {
-        dtl_prologue();
+        if constexpr (QLDS) {
+            dtl_q(0, dvs[1]);
+            dtl_q(1, dvs[2]);
+            dtl_k(tile_row(0), dks[0]);
+            dtl_k(tile_row(1), dks[1]);
+            dtl_v(tile_row(0), dvs[0]);
+            dtl_k(tile_row(2), dks[2]);
+        } else {
+            dtl_prologue();
+        }
         if constexpr (INT8 && !DUMP) {
 #pragma unroll
             for (int t = 0; t < NST; ++t) ksring[t] = kscale_at(t);
@@ -653,13 +690,28 @@ void fwd_kernel(const FwdParams p_in) {
         // (correctly rounded), q = clamp(rint(x * r), -127, 127); a == 0 gives
         // q = 0 and delta = 0.  Rows past the sequence repeat row S-1, which
         // leaves the maximum unchanged.
-        const char* qrow = static_cast<const char*>(p.q) +
-                           (bhq * S + static_cast<size_t>(geom::q_row(qi, S))) * (2 * D);
         h8 qraw[C::QSTEPS][2];
+        if constexpr (QLDS) {
+            // Q's copies have landed (those of K_0, K_1, V_0 and K_2 may not)
+            lds_stage_barrier<3 * DK::NI + VNI>();
+            const int rq = (wave & 1) * 32 + l32;   // row in the stage of this wave's half
+            const char* qs = ((wave >> 1) ? dvs[2] : dvs[1]) + rq * C::VROWG;
 #pragma unroll
-        for (int s = 0; s < C::QSTEPS; ++s)
+            for (int s = 0; s < C::QSTEPS; ++s)
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) qraw[s][hh] = *reinterpret_cast<const h8*>(qrow + C::q16_piece_offset(s, g, hh));
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int c = C::q16_piece_offset(s, g, hh) / 16;
+                    qraw[s][hh] = *reinterpret_cast<const h8*>(qs + ((c ^ DV::k_swz(rq)) << 4));
+                }
+        } else {
+            const char* qrow = static_cast<const char*>(p.q) +
+                               (bhq * S + static_cast<size_t>(geom::q_row(qi, S))) * (2 * D);
+#pragma unroll
+            for (int s = 0; s < C::QSTEPS; ++s)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+                    qraw[s][hh] = *reinterpret_cast<const h8*>(qrow + C::q16_piece_offset(s, g, hh));
+        }
         // |x| max on the fp16 bit patterns: with the sign bit cleared, the
         // integer order of finite values' patterns is the order of their
         // magnitudes (two per 32-bit word, packed 16-bit maxima)
@@ -679,7 +731,9 @@ void fwd_kernel(const FwdParams p_in) {
         for (int off = 32; off >= 1; off >>= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, off));
         __shared__ float qmax[4];
         if (lane == 0) qmax[wave] = amax;
-        __syncthreads();
+        // (LDS only: a full __syncthreads would also wait for the copies)
+        if constexpr (QLDS) lds_stage_barrier<63>();
+        else __syncthreads();
         const float a = __builtin_fmaxf(__builtin_fmaxf(qmax[0], qmax[1]), __builtin_fmaxf(qmax[2], qmax[3]));
         const float r = a == 0.0f ? 0.0f : __fdiv_rn(127.0f, a);
         qscale_fused = a == 0.0f ? 0.0f : __fdiv_rn(a, 127.0f);
@@ -709,6 +763,9 @@ void fwd_kernel(const FwdParams p_in) {
             __builtin_memcpy(&qf[s], w, 16);
         }
     }
+    // V_1 into the stage Q has left (every wave read its Q rows before the
+    // workgroup barrier of the block maximum)
+    if constexpr (QLDS) dtl_v(tile_row(1), dvs[1]);
 
     // Visible keys of a tile at n0 satisfy key_offset(mt, r) < lim for this lane.
     auto mask_limit = [&](int n0) { return geom::mask_limit(n0, S, qi, g, CAUSAL); };
@@ -731,8 +788,9 @@ void fwd_kernel(const FwdParams p_in) {
         constexpr bool kBiased = INT8 && !F8;   // INT32 scores read as biased fp32
         acc_t sc[2];
         if constexpr (DTL) {
-            // every prologue copy has landed (FP16: K_0; the later copies may be in flight)
-            lds_stage_barrier<QFIRST ? (NST == 3 ? 2 * DK::NI + 2 * VNI : DK::NI + VNI) : 0>();
+            // K_0 has landed (the INT8 kernel on INT8 Q: every prologue copy; the
+            // others leave the later copies in flight)
+            lds_stage_barrier<(QFIRST || QLDS) ? (NST == 3 ? 2 * DK::NI + 2 * VNI : DK::NI + VNI) : 0>();
             score_tile<D, INT8, F8, kBiased, true>(dks[0], qf, l32, g, sc);
         } else {
             sstore_k(0, kreg[0]);
@@ -965,20 +1023,21 @@ void fwd_kernel(const FwdParams p_in) {
         // must have landed (the copies of the last iteration may stay in
         // flight at NST = 3), then after the barrier K_{j+NST} goes into the
         // stage K_j left and V_{j+NST-1} into the stage V_{j-1} left.
-        // The K scale of tile j is loaded with tile j's copies (NST iterations
-        // earlier) into slot J of a small register ring: a wave-uniform load
-        // becomes a vector load once copies into LDS are in flight, and loaded
-        // late it would make the compiler wait for the whole copy queue.
+        // The K scale of tile j is loaded NST iterations ahead into slot J of a
+        // small register ring, at the end of an iteration: the next stage
+        // barrier's wait covers the scalar load, so no wait inside a tile does.
+        // (The barrier waits for the copies only: a K scale read with a
+        // vector load instead would just make it wait for one more copy.)
         auto dstep = [&](int j, auto j_tag) __attribute__((always_inline)) {
             constexpr int J = decltype(j_tag)::value;
             const float ksj = ksring[J];
             // (the score dump drains every copy: its global stores share the
             // vector-memory counter with the copies)
-            lds_stage_barrier<(NST == 3 && !DUMP) ? DK::NI + VNI + (INT8 ? 1 : 0) : 0>();
+            lds_stage_barrier<(NST == 3 && !DUMP) ? DK::NI + VNI : 0>();
             dtl_k(tile_row(j + NST), dks[J]);
-            if constexpr (INT8 && !DUMP) ksring[J] = kscale_at(j + NST);
             dtl_v(tile_row(j + NST - 1), dvs[(J + NST - 1) % NST]);
             if (j < nkt_w) compute(j, dks[(J + 1) % NST], (J + 1) % NST, dvs[J], ksj, std::true_type{});
+            if constexpr (INT8 && !DUMP) ksring[J] = kscale_at(j + NST);
         };
         if constexpr (DTL) {
             const int iters = geom::dtl_loop_iterations<NST>(nkt);

@@ -186,6 +186,28 @@ static void check_shape(int B, int Hq, int S, bool causal, bool dump, int tile_l
                 for (int v : seen_slot) REQUIRE(v == 1, "dtl slot written %d times", v);
             };
             for (int n0 : dk) check_tile(n0, St::KROWG, qk_head_bytes, false);
+            if (INT8 && !pv8) {
+                // fused-Q kernels: the block's fp16 Q rows q0 .. q0+127 copied
+                // as two 64-row halves into V-sized stages (K-style swizzle),
+                // then each lane's 16-byte pieces read back from its row
+                for (int h = 0; h < 2; ++h) check_tile(q0 + kTileN * h, St::VROWG, v_head_bytes, false);
+                const int rb = St::VROWG, cpr = rb / 16;
+                for (int h = 0; h < 2; ++h)
+                    for (int rq = 0; rq < kTileN; ++rq) {
+                        const int first = tile_first_row(q0 + kTileN * h, S);
+                        const int row = first + tile_lane_row(rq, first, S);
+                        REQUIRE(row == q_row(q0 + kTileN * h + rq, S), "fused q row %d", row);
+                        const int sw = rb == 256 ? Dtl<256>::k_swz(rq) : Dtl<128>::k_swz(rq);
+                        for (int s = 0; s < St::QSTEPS; ++s)
+                            for (int g = 0; g < 2; ++g)
+                                for (int hh = 0; hh < 2; ++hh) {
+                                    const int c = St::q16_piece_offset(s, g, hh) / 16;
+                                    const int pc = c ^ sw;
+                                    REQUIRE(c < cpr && pc >= 0 && pc < cpr && rq * rb + pc * 16 + 16 <= kTileN * rb,
+                                            "fused q lds read rq %d c %d pc %d", rq, c, pc);
+                                }
+                    }
+            }
             if (!pv8) {
                 for (int n0 : dvv) check_tile(n0, St::VROWG, v_head_bytes, true);
             } else {
