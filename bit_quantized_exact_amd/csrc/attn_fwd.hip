@@ -1028,14 +1028,22 @@ void fwd_kernel(const FwdParams p_in) {
         // barrier's wait covers the scalar load, so no wait inside a tile does.
         // (The barrier waits for the copies only: a K scale read with a
         // vector load instead would just make it wait for one more copy.)
+        // Tiles past the item's last one are not copied; the barrier after an
+        // iteration that skipped a copy waits for every copy (its count
+        // assumes the full set of copies after the awaited ones).
         auto dstep = [&](int j, auto j_tag) __attribute__((always_inline)) {
             constexpr int J = decltype(j_tag)::value;
             const float ksj = ksring[J];
             // (the score dump drains every copy: its global stores share the
             // vector-memory counter with the copies)
-            lds_stage_barrier<(NST == 3 && !DUMP) ? DK::NI + VNI : 0>();
-            dtl_k(tile_row(j + NST), dks[J]);
-            dtl_v(tile_row(j + NST - 1), dvs[(J + NST - 1) % NST]);
+            if constexpr (NST == 3 && !DUMP) {
+                if (j + NST <= nkt) lds_stage_barrier<DK::NI + VNI>();
+                else lds_stage_barrier<0>();
+            } else {
+                lds_stage_barrier<0>();
+            }
+            if (j + NST < nkt) dtl_k(tile_row(j + NST), dks[J]);
+            if (j + NST - 1 < nkt) dtl_v(tile_row(j + NST - 1), dvs[(J + NST - 1) % NST]);
             if (j < nkt_w) compute(j, dks[(J + 1) % NST], (J + 1) % NST, dvs[J], ksj, std::true_type{});
             if constexpr (INT8 && !DUMP) ksring[J] = kscale_at(j + NST);
         };
@@ -1056,6 +1064,11 @@ void fwd_kernel(const FwdParams p_in) {
             for (int j = 0; j < nkt; ++j) step(j, std::integral_constant<int, 0>{});
         }
 
+        // No copy into LDS may still be landing when the workgroup ends or its
+        // next item's copies go out, and every wave must be done with the
+        // stages: drained here, before the output stores, so that nothing
+        // waits for the stores (the next item's loads go out behind them).
+        if constexpr (DTL) lds_stage_barrier<0>();
         // (stored after the loop: a global store ahead of it would keep the
         // compiler from using scalar loads for the per-tile K scales)
         if constexpr (QF16)
@@ -1089,9 +1102,6 @@ void fwd_kernel(const FwdParams p_in) {
                 if (p.lse && g == 0) p.lse[bhq * S + qi] = (m_run + __builtin_log2f(l_tot)) * kLn2;
             }
         }
-        // no copy into LDS may still be landing when the workgroup ends (the
-        // last iterations' copies of tiles past the end drain under the stores)
-        if constexpr (DTL) lds_stage_barrier<0>();
     }
     }   // work items
 }
