@@ -141,6 +141,21 @@ __device__ __forceinline__ int row_max_i(int x) {
     const auto r = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(x), static_cast<unsigned>(x), false, false);
     return max(static_cast<int>(r[0]), static_cast<int>(r[1]));
 }
+// Maximum of the non-negative values v over the 64 lanes of the wave, read
+// from lane 63: prefix maxima within each 16-lane row by the DPP row shifts
+// 1, 2, 4, 8, then the row broadcasts of lanes 15 and 31 into the rows above
+// (lanes shifted in from outside a row, and rows outside a broadcast's row
+// mask, take 0, which leaves a maximum of non-negative values unchanged).
+// All VALU: no LDS round trip per step as with cross-lane shuffles.
+__device__ __forceinline__ unsigned wave_max_nonneg(unsigned v) {
+    v = max(v, static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x111, 0xf, 0xf, true)));
+    v = max(v, static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x112, 0xf, 0xf, true)));
+    v = max(v, static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x114, 0xf, 0xf, true)));
+    v = max(v, static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x118, 0xf, 0xf, true)));
+    v = max(v, static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x142, 0xa, 0xf, false)));
+    v = max(v, static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x143, 0xc, 0xf, false)));
+    return static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
 __device__ __forceinline__ float row_sum(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
@@ -725,10 +740,9 @@ void fwd_kernel(const FwdParams p_in) {
                 for (int e = 0; e < 4; ++e)
                     mx2 = __builtin_elementwise_max(mx2, __builtin_bit_cast(u16x2, static_cast<unsigned>(w[e]) & 0x7fff7fffu));
             }
-        const unsigned short mx = mx2[0] > mx2[1] ? mx2[0] : mx2[1];
-        float amax = static_cast<float>(__builtin_bit_cast(_Float16, mx));
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, off));
+        // (the wave's maximum pattern, then its value: the same order)
+        const unsigned mxw = wave_max_nonneg(mx2[0] > mx2[1] ? mx2[0] : mx2[1]);
+        const float amax = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<unsigned short>(mxw)));
         __shared__ float qmax[4];
         if (lane == 0) qmax[wave] = amax;
         // (LDS only: a full __syncthreads would also wait for the copies)
