@@ -56,21 +56,25 @@ __device__ __forceinline__ float half_bits_to_float(unsigned h) {
 // the K quantiser to add them itself (no mean launch).
 constexpr int kColsumThreads = 512;
 constexpr int kMaxPartials = 32;
-template <int D>
+// The columns are split over NCS workgroups (blockIdx.z: columns
+// z*D/NCS .. +D/NCS), so that a group of chunks spreads over NCS workgroups.
+template <int D, int NCS = 1>
 __global__ __launch_bounds__(kColsumThreads) void k_colsum_kernel(const uint16_t* __restrict__ k, int S,
                                                                   int cps, int npart,
                                                                   long long* __restrict__ partial) {
-    constexpr int CPR = D / 8;                  // 16-byte chunks per row
+    constexpr int DW = D / NCS;                 // columns of this workgroup
+    constexpr int CPR = DW / 8;                 // 16-byte chunks per row
     constexpr int RG = kColsumThreads / CPR;    // row groups
     constexpr int RPT = kSumChunk / RG;         // rows per thread per chunk
     static_assert(kSumChunk % RG == 0 && 512 * RPT <= 4096 && 4096.0 * 65536.0 * 16777216.0 < 9007199254740992.0,
                   "exact fp64 thread sums");
-    __shared__ long long red[RG][D];
+    __shared__ long long red[RG][DW];
     const int t = threadIdx.x;
     const int cc = t % CPR, rg = t / CPR;
     const int grp = blockIdx.x;
     const size_t bk = blockIdx.y;
-    const uint16_t* base = k + bk * static_cast<size_t>(S) * D + cc * 8;
+    const int col0 = static_cast<int>(blockIdx.z) * DW;
+    const uint16_t* base = k + bk * static_cast<size_t>(S) * D + col0 + cc * 8;
     double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     // the rows of chunk c of the group (rows past the sequence read the last row)
     auto load = [&](int c, i4x (&v)[RPT]) __attribute__((always_inline)) {
@@ -110,17 +114,34 @@ __global__ __launch_bounds__(kColsumThreads) void k_colsum_kernel(const uint16_t
 #pragma unroll
     for (int e = 0; e < 8; ++e) red[rg][cc * 8 + e] = static_cast<long long>(__builtin_ldexp(acc[e], 24));
     __syncthreads();
-    if (t < D) {
+    if (t < DW) {
         long long s = 0;
 #pragma unroll
         for (int g = 0; g < RG; ++g) s += red[g][t];
-        partial[(bk * npart + grp) * D + t] = s;
+        partial[(bk * npart + grp) * D + col0 + t] = s;
     }
 }
 
+// Maximum of the non-negative values v over the 64 lanes of the wave, read
+// from lane 63: prefix maxima within each 16-lane row by the DPP row shifts
+// 1, 2, 4, 8, then the row broadcasts of lanes 15 and 31 into the rows above
+// (lanes shifted in from outside a row, and rows outside a broadcast's row
+// mask, take 0, which leaves a maximum of non-negative values unchanged).
+// Non-negative floats order as their bit patterns do as unsigned integers.
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+    unsigned v = __float_as_uint(x);
+    v = max(v, static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x111, 0xf, 0xf, true)));
+    v = max(v, static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x112, 0xf, 0xf, true)));
+    v = max(v, static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x114, 0xf, 0xf, true)));
+    v = max(v, static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x118, 0xf, 0xf, true)));
+    v = max(v, static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x142, 0xa, 0xf, false)));
+    v = max(v, static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x143, 0xc, 0xf, false)));
+    return __uint_as_float(static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(v), 63)));
+}
+
+// Maximum of the non-negative v over the 256-thread workgroup (through red[4]).
 __device__ __forceinline__ float block_max(float v, float* red) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    v = wave_max_nonneg(v);
     const int wave = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) red[wave] = v;
     __syncthreads();
@@ -405,8 +426,10 @@ int launch_quantize_d(const attn_shape& s, const void* q, const void* k, int8_t*
     // sums per (b, kv-head) remain for the K quantiser to add
     const int cps = ceil_div(ws.nchunk, kMaxPartials);
     const int npart = ceil_div(ws.nchunk, cps);
-    hipLaunchKernelGGL(k_colsum_kernel<D>, dim3(npart, BH_kv), dim3(kColsumThreads), 0, st, kk, S, cps, npart,
-                       ws.partial);
+    // (head_dim 128: the columns in two halves, two workgroups per group of chunks)
+    constexpr int NCS = D == 128 ? 2 : 1;
+    hipLaunchKernelGGL((k_colsum_kernel<D, NCS>), dim3(npart, BH_kv, NCS), dim3(kColsumThreads), 0, st, kk, S, cps,
+                       npart, ws.partial);
     const int nkb = ceil_div(S, kBK), nqb = ceil_div(S, kBQ);
     // K blocks per quantiser workgroup: one while that leaves at most 1024
     // workgroups, else up to 8 (each workgroup adds the partial sums once
