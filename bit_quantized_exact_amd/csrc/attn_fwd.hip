@@ -39,9 +39,13 @@
 //     global_load_lds_dwordx4 (no VGPRs, no LDS store instructions) into
 //     three (FP16 at D = 128: two) stages per tile kind; the stages are
 //     unpadded and XOR-swizzled in 16-byte chunks so that the MFMA operand
-//     reads and the transposing reads are free of bank conflicts.  The
-//     INT32 score dump, and tile-masked lists longer than the LDS copy of
-//     the list holds, stage through registers into padded rows instead.
+//     reads and the transposing reads are free of bank conflicts.  Tiles
+//     past an item's last key tile are not copied.  Tile-masked lists longer
+//     than the LDS copy of the list holds stage through registers into padded
+//     rows instead.  The per-tile K scales are scalar loads, so the stage
+//     barriers count copies only.  The INT8 kernel that quantises fp16 Q
+//     itself stages Q through LDS too, ahead of the first tiles' copies, and
+//     quantises it while they land.
 //   * Lazy rescaling: the running maximum is only raised (and O, l rescaled)
 //     when a tile's maximum exceeds it by more than 2^8; otherwise the stale
 //     maximum is kept, weights stay <= 2^8 (exact in fp16 range), and the
@@ -52,7 +56,9 @@
 //   * Workgroups are launched XCD-aware: consecutive hardware block ids go
 //     round-robin over the 8 XCDs, so work items are numbered such that each
 //     XCD receives a contiguous range of (batch, head) pairs ordered by kv
-//     head; the q-heads of one GQA group then share K/V in that XCD's L2.
+//     head; the q-heads of one GQA group then share K/V in that XCD's L2
+//     (where a kv-head's K and V exceed the L2, the group's q-heads at the
+//     same query tile are adjacent, so that they read each tile together).
 //     Causal launches start with the heaviest (last) query tiles, and with
 //     many items they give each workgroup two (a heavy and a light one, in
 //     the snake order of geom::make_sched): the workgroups then carry equal
