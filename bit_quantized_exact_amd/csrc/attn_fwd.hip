@@ -239,13 +239,17 @@ typedef const __attribute__((address_space(3))) char* lds_cptr;
 // wave reads at each k-step, given for query-row block 0 (block 1 lies 32
 // rows further: the swizzle repeats every 32 rows at these row sizes).
 template <int D, bool INT8, bool BIASED, int N, typename QF, typename ACC>
-__device__ __forceinline__ void score_tile_at(const lds_cptr (&ka)[N], const QF* qf, ACC* acc) {
+__device__ __forceinline__ void score_tile_at(const lds_cptr (&ka)[N], const QF* qf, ACC* acc,
+                                              const ACC* init = nullptr) {
     using C = Cfg<D, INT8, false>;
     static_assert(N == C::QSTEPS, "one address per k-step");
     static_assert(32 % geom::Dtl<C::KROWG>::RPL == 0 && (32 / geom::Dtl<C::KROWG>::RPL) % geom::Dtl<C::KROWG>::CPR == 0,
                   "the K swizzle must repeat every 32 rows");
     static_assert(!BIASED || INT8, "the bias applies to INT32 accumulators");
-    if constexpr (BIASED) {
+    if (init) {
+        acc[0] = *init;
+        acc[1] = *init;
+    } else if constexpr (BIASED) {
         acc[0] = kI8BiasBits;
         acc[1] = kI8BiasBits;
     } else {
@@ -807,6 +811,14 @@ void fwd_kernel(const FwdParams p_in) {
         // depth 2, K_2 and V_1 into the second register set) ----
         constexpr bool kBiased = INT8 && !F8;   // INT32 scores read as biased fp32
         acc_t sc[2];
+        // The accumulators' starting block (the bias bits), held in registers
+        // for the whole item and opaque to the compiler, which would otherwise
+        // re-create it with eight 64-bit moves per tile.
+        acc_t bias_blk{};
+        if constexpr (kBiased && KADDR) {
+            bias_blk = kI8BiasBits;
+            asm volatile("" : "+v"(bias_blk));
+        }
         if constexpr (DTL) {
             // K_0 has landed (the INT8 kernel on INT8 Q: every prologue copy; the
             // others leave the later copies in flight)
@@ -928,7 +940,8 @@ void fwd_kernel(const FwdParams p_in) {
                 // row maxima (same-run A/B: +3-4 % on the 8192-token prefill).
                 __builtin_amdgcn_s_setprio(1);
                 acc_t sn[2];
-                if constexpr (KADDR && SWZ) score_tile_at<D, INT8, kBiased>(kaddr[kst], qf, sn);
+                if constexpr (KADDR && SWZ)
+                    score_tile_at<D, INT8, kBiased>(kaddr[kst], qf, sn, kBiased ? &bias_blk : nullptr);
                 else score_tile<D, INT8, F8, kBiased, SWZ>(ksn, qf, l32, g, sn);
 
                 const float m_eff = BMASK && m_run == -INFINITY ? 0.0f : m_run;   // (masked rows: weights 0)
