@@ -29,7 +29,9 @@ of the 8192-token prefill (1024 anchor, 2048 passing, 5120 local tokens).
 
 `roofline` describes the dominant kernel of the step; `mfma_loop` gives, as
 context for its published peak, the rate a dense MFMA loop sustains on this
-device (libattn_probe.so); `cpu_baseline` times the CPU oracle (fp64, plain
+device (libattn_probe.so), and `hbm_read` the bandwidth a plain streaming read
+of a 4 GiB buffer reaches, context for the 8 TB/s of the HBM-bound kernels;
+`cpu_baseline` times the CPU oracle (fp64, plain
 loops) on a bounded, seeded sample of the headline workload's query rows, on
 this machine's host cores, and `parity_sample` compares the GPU outputs with
 it on those rows.
@@ -401,7 +403,58 @@ def run_workload(name, steps, warmup, cpu=False, cpu_seconds=15.0, configs=True,
             torch.cuda.empty_cache()
     rec["paths"]["decode"] = run_decode()
     rec["mfma_loop"] = run_mfma_loop()
+    rec["hbm_read"] = run_hbm_read()
     return rec
+
+
+def run_hbm_read(nbytes=1 << 32, reps=10, per_cu=(1, 2, 3, 4)):
+    """Practical HBM read bandwidth of this device: streaming passes over a
+    4 GiB buffer (16 times the 256 MB Infinity Cache, so the reads come from
+    HBM; attn_probe_hbm_read: non-temporal 16-byte loads, four in flight per
+    thread), with 1 to 4 workgroups of 256 threads per compute unit (more bytes
+    in flight per compute unit measured slower), each timed with HIP events
+    on the launch stream after a clock warm-up; the best shape is reported.
+    Context for the HBM-bound kernels (decode, quantisation), whose
+    `frac_hbm_peak` stays against the published 8 TB/s."""
+    import ctypes
+
+    import torch
+
+    from bit_quantized_exact_amd import probe
+
+    L = probe.lib()
+    cus = ctypes.c_int(0)
+    if L.attn_probe_compute_units(ctypes.byref(cus)) != 0 or cus.value <= 0:
+        return None
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(max(per_cu) * cus.value * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def time_shape(blocks):
+        def launch():
+            st = L.attn_probe_hbm_read(ctypes.c_void_p(buf.data_ptr()), nbytes, blocks,
+                                       ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+            if st != 0:
+                raise RuntimeError(f"attn_probe_hbm_read failed: {st}")
+
+        clock_warm(launch, min_ms=50, batch=2)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            launch()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    shapes = {n: time_shape(n * cus.value) for n in per_cu}
+    best = min(shapes, key=shapes.get)
+    ms = shapes[best]
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del buf, sink
+    torch.cuda.empty_cache()
+    return {"bytes": nbytes, "workgroups_per_cu": best, "ms": round(ms, 4), "gbs": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "gbs_by_workgroups_per_cu": {str(n): round(nbytes / (t * 1e-3) / 1e9, 1) for n, t in shapes.items()}}
 
 
 def run_mfma_loop(iters=20000, reps=5):

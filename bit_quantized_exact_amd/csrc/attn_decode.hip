@@ -24,7 +24,8 @@
 //     loads in flight while the current tile is computed;
 //   * K tiles go straight from HBM into the MFMA operand registers (the
 //     transposed form S^T = K Q^T takes K rows as the A operand); V tiles pass
-//     through padded LDS for the transposing reads of O^T += V^T P^T;
+//     through padded LDS for the transposing reads of O^T += V^T P^T, loaded
+//     with the non-temporal (streaming) cache policy;
 //   * each workgroup leaves its unnormalised partial O, running maximum and
 //     sum; a combine kernel rescales and sums the ranges (exactly as the
 //     online softmax merges tiles) and writes O and the log-sum-exp.
@@ -134,13 +135,18 @@ void decode_kernel(const DecParams p) {
 #pragma unroll
         for (int s = 0; s < C::QSTEPS; ++s) dst[s] = *reinterpret_cast<const frag_t*>(row + C::frag_offset(s, g));
     };
+    // V rows are read whole by consecutive lanes and never again: non-temporal
+    // loads (the streaming cache policy).  K keeps the default policy: each
+    // K load instruction touches 32 bytes of 32 different rows, and the rows'
+    // other bytes come with the next k-steps' loads, which the default policy
+    // serves from the cache lines the first one brought in.
     auto gload_v = [&](int t) {
 #pragma unroll
         for (int i = 0; i < C::VPT; ++i) {
             const int c = lane + dec::kThreads * i;
             const int r = c / C::VCPR;
-            vr[i] = *reinterpret_cast<const i4x*>(vg + static_cast<size_t>(dec::key_row(t * dec::kTile, r, Sk)) * C::VROWG +
-                                                  (c % C::VCPR) * 16);
+            const char* src = vg + static_cast<size_t>(dec::key_row(t * dec::kTile, r, Sk)) * C::VROWG + (c % C::VCPR) * 16;
+            vr[i] = __builtin_nontemporal_load(reinterpret_cast<const i4x*>(src));
         }
     };
     auto sstore_v = [&]() {

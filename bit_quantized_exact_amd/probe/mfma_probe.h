@@ -2,9 +2,9 @@
  * mfma_probe.h - measurement helpers of libattn_probe.so, a small library
  * of its own beside libattn.so.  They are not part of the attention path and
  * not part of its C ABI: the benchmark uses them to report the sustained
- * matrix-core rate of the device next to the published peaks, so that a
- * kernel's fraction of the peak can be read against what a dense MFMA loop
- * reaches on the same part.
+ * matrix-core rate and the streaming read bandwidth of the device next to the
+ * published peaks, so that a kernel's fraction of a peak can be read against
+ * what a dense MFMA loop or a plain read reaches on the same part.
  */
 #ifndef ATTN_MFMA_PROBE_H
 #define ATTN_MFMA_PROBE_H
@@ -25,6 +25,16 @@ extern "C" {
  * kind 3 reports kind 2's count).  Returns 0, -1 for a bad argument (nothing
  * launched), -3 when the launch failed. */
 int attn_probe_mfma(int kind, int blocks, int iters, float* sink, double* ops, void* stream);
+
+/* Streaming read of `bytes` bytes of DEVICE memory at `buf` (16-byte
+ * aligned, bytes a multiple of 16, owned by the caller): `blocks` workgroups
+ * of 256 threads read it once in 16-byte non-temporal loads, four in flight
+ * per thread, and each thread writes the XOR of what it read, as a float, to `sink`
+ * (DEVICE memory, blocks * 256 floats).  The practical read bandwidth of the
+ * part, reported beside the 8 TB/s published peak for the HBM-bound kernels
+ * (decode, quantisation).  Returns 0, -1 for a bad argument (nothing
+ * launched), -3 when the launch failed. */
+int attn_probe_hbm_read(const void* buf, unsigned long long bytes, int blocks, float* sink, void* stream);
 
 /* Compute units of the current device into *cus (HOST).  Returns 0, -1 for a
  * NULL pointer or no device, -3 when the query failed. */

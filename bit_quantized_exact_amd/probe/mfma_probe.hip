@@ -7,7 +7,8 @@
 // v_mfma_i32_32x32x32_i8), so the matrix pipe never waits on a result; the
 // accumulators are summed into one value per lane at the end (so the loop is
 // not removed).  Two 256-thread workgroups per compute unit give two waves
-// per SIMD, as in the forward kernels.
+// per SIMD, as in the forward kernels.  A streaming read of a large buffer
+// gives the practical HBM read bandwidth the same way.
 #include "mfma_probe.h"
 
 #include <hip/hip_runtime.h>
@@ -108,7 +109,35 @@ __global__ __launch_bounds__(256) void mfma_valu_mix(int iters, float* __restric
     sink[static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x] = s;
 }
 
+// One pass over n16 16-byte chunks: thread t of the grid reads chunks
+// t, t + T, t + 2T, ... (T threads in all), four loads in flight per round,
+// with the non-temporal (streaming) cache policy.
+__global__ __launch_bounds__(256) void hbm_read(const i4x* __restrict__ p, unsigned long long n16,
+                                                float* __restrict__ sink) {
+    const unsigned long long T = static_cast<unsigned long long>(gridDim.x) * blockDim.x;
+    unsigned long long i = static_cast<unsigned long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+    i4x x = {0, 0, 0, 0};
+    for (; i + 3 * T < n16; i += 4 * T) {
+        const i4x a = __builtin_nontemporal_load(p + i), b = __builtin_nontemporal_load(p + i + T);
+        const i4x c = __builtin_nontemporal_load(p + i + 2 * T), d = __builtin_nontemporal_load(p + i + 3 * T);
+        x ^= a ^ b ^ c ^ d;
+    }
+    for (; i < n16; i += T) x ^= __builtin_nontemporal_load(p + i);
+    sink[static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x] =
+        static_cast<float>(x[0] ^ x[1] ^ x[2] ^ x[3]);
+}
+
 }  // namespace
+
+extern "C" int attn_probe_hbm_read(const void* buf, unsigned long long bytes, int blocks, float* sink,
+                                   void* stream) {
+    if (!buf || !sink || blocks <= 0 || bytes == 0 || bytes % 16 != 0 ||
+        reinterpret_cast<unsigned long long>(buf) % 16 != 0)
+        return -1;
+    hipLaunchKernelGGL(hbm_read, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const i4x*>(buf), bytes / 16, sink);
+    return hipGetLastError() == hipSuccess ? 0 : -3;
+}
 
 extern "C" int attn_probe_mfma(int kind, int blocks, int iters, float* sink, double* ops, void* stream) {
     if (kind < 0 || kind > 3 || blocks <= 0 || iters <= 0 || !sink) return -1;

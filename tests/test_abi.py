@@ -419,3 +419,9 @@ def test_mfma_probe_rejects_bad_arguments():
     assert L.attn_probe_mfma(1, 1, 0, FAKE, ctypes.byref(ops), None) == -1    # no iterations
     assert L.attn_probe_mfma(0, 1, 1, None, ctypes.byref(ops), None) == -1    # no sink
     assert L.attn_probe_compute_units(None) == -1
+    assert L.attn_probe_hbm_read(None, 16, 1, FAKE, None) == -1                # no buffer
+    assert L.attn_probe_hbm_read(FAKE, 0, 1, FAKE, None) == -1                 # no bytes
+    assert L.attn_probe_hbm_read(FAKE, 24, 1, FAKE, None) == -1                # not whole 16-byte chunks
+    assert L.attn_probe_hbm_read(FAKE, 16, 0, FAKE, None) == -1                # no blocks
+    assert L.attn_probe_hbm_read(FAKE, 16, 1, None, None) == -1                # no sink
+    assert L.attn_probe_hbm_read(MISALIGNED, 16, 1, FAKE, None) == -1          # misaligned
