@@ -516,11 +516,16 @@ def run_mfma_loop(iters=20000, reps=5):
     return out
 
 
-def run_decode(name="decode_gqa", reps=20, warm_ms=None):
+def run_decode(name="decode_gqa", reps=20, warm_ms=None, cold_reps=15):
     """KV-cache decode (one query per sequence over a cached context): the
     INT8 kernel (cache quantised once beforehand) and the FP16 kernel, each
     timed with HIP events; HBM-bound, so reported as GB/s of algorithmic bytes
-    (the cache read once, Q read and O written once) against 8 TB/s."""
+    (the cache read once, Q read and O written once) against 8 TB/s.  `us`
+    and `gbs` time calls back to back, where part of a cache that does not
+    fill the 256 MB Infinity Cache can stay there from one call to the next;
+    `us_cold` and `gbs_cold` time single calls, each after a 1 GiB read has
+    evicted the cache (the case of a model whose layers each read their own
+    cache), median of `cold_reps`."""
     import torch
 
     import bit_quantized_exact_amd as A
@@ -536,7 +541,8 @@ def run_decode(name="decode_gqa", reps=20, warm_ms=None):
     stream = torch.cuda.current_stream()
     f8 = lambda: A.decode_int8(qd, kz, vd, causal=w.causal, out=o8, workspace=ws8)
     f16 = lambda: A.decode_fp16(qd, kd, vd, causal=w.causal, out=o16, workspace=ws8)
-    res = {}
+    res, cold = {}, {}
+    evict = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
     for tag, fn in (("int8", f8), ("fp16", f16)):
         clock_warm(fn, min_ms=CLOCK_WARM_MS if warm_ms is None else warm_ms, batch=16)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -546,6 +552,17 @@ def run_decode(name="decode_gqa", reps=20, warm_ms=None):
         e1.record(stream)
         torch.cuda.synchronize()
         res[tag] = e0.elapsed_time(e1) / reps
+        ts = []
+        for _ in range(cold_reps):
+            torch.sum(evict, dtype=torch.int64)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        cold[tag] = float(np.median(ts))
+    del evict
     B, Hq, Hkv, Sq, Sk, D = w.batch, w.heads_q, w.heads_kv, w.n_q, w.seq, w.head_dim
     qo = 2 * 2 * B * Hq * Sq * D
     bytes8 = B * Hkv * Sk * D + 2 * B * Hkv * Sk * D + qo + 4 * B * Hkv * math.ceil(Sk / 64)
@@ -555,8 +572,11 @@ def run_decode(name="decode_gqa", reps=20, warm_ms=None):
     for tag, nbytes in (("int8", bytes8), ("fp16", bytes16)):
         ms = res[tag]
         gbs = nbytes / (ms * 1e-3) / 1e9
+        gbs_c = nbytes / (cold[tag] * 1e-3) / 1e9
         out[tag] = {"us": round(ms * 1e3, 2), "algorithmic_bytes": nbytes, "gbs": round(gbs, 1),
                     "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                    "us_cold": round(cold[tag] * 1e3, 2), "gbs_cold": round(gbs_c, 1),
+                    "frac_hbm_peak_cold": round(gbs_c / HBM_PEAK_GBS, 4),
                     "tokens_per_s": round(B * Sq / (ms * 1e-3), 1),
                     "tflops": round(w.flops() / (ms * 1e-3) / 1e12, 2)}
     out["int8_speedup_over_fp16"] = round(res["fp16"] / res["int8"], 3)
