@@ -233,6 +233,10 @@ def config_entry(w, t):
                        "gbs": round(by["quantize_k"] / (t["ms_q"] * 1e-3) / 1e9, 1),
                        "frac_hbm_peak": round(by["quantize_k"] / (t["ms_q"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "int8_speedup_over_fp16": round(t["ms_16"] / (t["ms_q"] + t["ms_8"]), 3),
+        # HBM bytes per call over the algorithmic bytes, from the committed
+        # counter summaries of this workload (null where none or stale)
+        "traffic_over_algorithmic": {tag: (None if tr is None else round(tr / by[tag], 3))
+                                     for tag, tr in ((k, counters_for(k, w.name)) for k in by)},
     }
 
 
