@@ -213,6 +213,17 @@ def test_int8_workloads_sampled(name):
     _int8_check(w, q, k, v, rows=rows)
 
 
+def test_fp16_and_int8_at_a_million_tokens_sampled():
+    """2^20 tokens, causal, two q-heads on one kv-head, head_dim 64: per-lane
+    offsets, tile counts and the two-items-per-workgroup schedule at a long
+    sequence; sampled rows against the oracle (FP16 and INT8 paths)."""
+    w = small_workload(1, 2, 1, 1 << 20, 64, True, seed=81)
+    q, k, v = make_qkv(w)
+    rows = sample_rows(w.seq, 8, seed=81)
+    _fp16_check(w, q, k, v, rows=rows)
+    _int8_check(w, q, k, v, rows=rows)
+
+
 # --------------------------------------------------------------------------
 # lse, invariants, determinism, wrappers
 # --------------------------------------------------------------------------

@@ -109,3 +109,38 @@ def test_quantize_k_mean_exact_under_cancellation():
     ref = O.quantize_qk(q, k)
     exact = k[0, 0, :, 2].astype(np.float64).sum() / S
     assert ref["k_mean"][0, 0, 2] == np.float32(exact)
+
+
+def test_quantize_bitexact_at_the_maximum_sequence():
+    """ATTN_MAX_SEQ = 2^22 tokens, the longest sequence the ABI accepts and the
+    length up to which the fixed-point channel sums are exact: every output
+    bit-exact against the oracle (one q-head on one kv-head, head_dim 128)."""
+    w = small_workload(1, 1, 1, 1 << 22, 128, False, seed=71)
+    q, k, _ = make_qkv(w)
+    _compare(w, q, k)
+
+
+def test_k_mean_exact_at_the_maximum_sequence_extremes():
+    """At 2^22 tokens, channels whose exact means are known without the oracle
+    (which refuses sums this large): constant +65504, constant -65504, the
+    smallest subnormal 2^-24 everywhere, and one 65504 among 2^-24s (a sum
+    that loses every small term in any fp32 order).  The mean is the exact
+    sum, rounded once to fp64, divided by S and rounded to fp32."""
+    S = 1 << 22
+    tiny = 2.0 ** -24
+    k = np.zeros((1, 1, S, 64), dtype=np.float16)
+    k[0, 0, :, 0] = np.float16(65504.0)
+    k[0, 0, :, 1] = np.float16(-65504.0)
+    k[0, 0, :, 2] = np.float16(tiny)
+    k[0, 0, :, 3] = np.float16(tiny)
+    k[0, 0, 0, 3] = np.float16(65504.0)
+    case("quantize_k 2^22 tokens, extreme channel sums")
+    got = A.quantize_k(dev(k))
+    torch.cuda.synchronize()
+    mean = host(got["k_mean"])[0, 0]
+    want = np.zeros(64, dtype=np.float32)
+    want[0], want[1], want[2] = 65504.0, -65504.0, np.float32(tiny)
+    want[3] = np.float32((65504.0 + (S - 1) * tiny) / S)
+    assert want[3] != np.float32(65504.0 / S)          # the small terms matter
+    np.testing.assert_array_equal(mean.view(np.uint32), want.view(np.uint32))
+
