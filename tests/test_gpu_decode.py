@@ -127,3 +127,14 @@ def test_decode_rows_match_prefill_rows():
     torch.cuda.synchronize()
     diff = (dec.float() - pre[:, :, Sk - Sq:].float()).abs().max().item()
     assert diff <= 2 * FP16_MAX_ABS, diff
+
+
+def test_decode_at_the_maximum_cache():
+    """A cache of ATTN_MAX_SEQ = 2^22 keys (1 GiB each of K and V at head_dim
+    128): 1024 key splits merged by the combine kernel; the cache quantisation
+    bit-exact, both decode kernels against the oracle as above."""
+    w = _w((1, 4, 1, 3, 1 << 22, 128, True, None), seed=977)
+    q, k, v = make_qkv(w)
+    _int8_check(w, q, k, v)
+    _fp16_check(w, q, k, v)
+
