@@ -224,6 +224,17 @@ def test_fp16_and_int8_at_a_million_tokens_sampled():
     _int8_check(w, q, k, v, rows=rows)
 
 
+def test_fp16_and_int8_at_the_maximum_sequence_sampled():
+    """ATTN_MAX_SEQ = 2^22 tokens, causal, head_dim 128 (1 GiB per K and V
+    head, the largest per-lane copy offsets): sampled rows against the oracle
+    (FP16 and INT8 paths)."""
+    w = small_workload(1, 1, 1, 1 << 22, 128, True, seed=83)
+    q, k, v = make_qkv(w)
+    rows = sample_rows(w.seq, 6, seed=83)
+    _fp16_check(w, q, k, v, rows=rows)
+    _int8_check(w, q, k, v, rows=rows)
+
+
 # --------------------------------------------------------------------------
 # lse, invariants, determinism, wrappers
 # --------------------------------------------------------------------------
