@@ -81,7 +81,7 @@ def parse():
     ap.add_argument("--config-steps", type=int, default=10,
                     help="timed steps per workload in paths.configs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (HBM counter calibration)")
@@ -240,7 +240,7 @@ def config_entry(w, t):
     }
 
 
-def run_workload(name, steps, warmup, cpu=False, cpu_seconds=15.0, configs=True, config_steps=10):
+def run_workload(name, steps, warmup, cpu=False, cpu_seconds=12.0, configs=True, config_steps=10):
     import torch
 
     import bit_quantized_exact_amd as A
@@ -637,10 +637,12 @@ def cpu_baseline(w, q, k, v, o8, o16, target_s, extra=None):
         out = O.attention(q, k, v, causal=w.causal, rows=rows, nthreads=threads)
         return out, time.perf_counter() - t
 
-    # calibrate on 16 rows, then size the sample for about target_s seconds
-    cal = np.sort(rng.choice(w.seq, min(w.seq, 16), replace=False)).astype(np.int32)
+    # calibrate on 128 rows (several per thread, so that the threads' share
+    # is as even as in the sample), then size the sample for about target_s
+    ncal = min(w.seq, 128)
+    cal = np.sort(rng.choice(w.seq, ncal, replace=False)).astype(np.int32)
     _, tc = timed(cal)
-    n = int(min(w.seq, max(16, 16 * target_s / max(tc, 1e-3))))
+    n = int(min(w.seq, max(ncal, ncal * target_s / max(tc, 1e-3))))
     rows = np.sort(rng.choice(w.seq, n, replace=False)).astype(np.int32)
     out, dt = timed(rows)
     fl = row_flop(rows)
